@@ -1,0 +1,409 @@
+// Host encoder and the host-only entry points of the C ABI.
+//
+// Follows the "neural-weight-compression 0.9.0" PyPI page, "How it works":
+// byte planes (raw mantissa byte, coded exponent/sign byte), per-matrix
+// frequency ranking, unary rank code with a raw sign bit and an escape; and
+// the "Qwen3-4B-NWC-fp8" model card for fp8 bytes coded whole.  The stream
+// layout (64-row work items, one lane column per row) is described in
+// nwc_format.h.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "nwc_check.h"
+
+namespace {
+
+struct CodeTable {
+  uint32_t val[256];  // codeword bits, first stream bit in bit 0
+  uint8_t len[256];
+};
+
+int worker_count() {
+  if (const char *s = std::getenv("NWC_ENCODE_THREADS")) {
+    int v = std::atoi(s);
+    if (v > 0) return std::min(v, 256);
+  }
+  unsigned hc = std::thread::hardware_concurrency();
+  return (int)std::max(1u, std::min(hc, 64u));
+}
+
+// Runs f(begin, end) over [0, n) split across worker threads.
+template <class F>
+void parallel_for(int64_t n, F f) {
+  const int t = (int)std::min<int64_t>(worker_count(), std::max<int64_t>(n, 1));
+  if (t <= 1) {
+    f((int64_t)0, n);
+    return;
+  }
+  std::vector<std::thread> th;
+  th.reserve(t);
+  for (int i = 0; i < t; ++i) {
+    const int64_t b = n * i / t, e = n * (i + 1) / t;
+    th.emplace_back([=] { f(b, e); });
+  }
+  for (auto &x : th) x.join();
+}
+
+// Frequency rank: count descending, equal counts by ascending symbol.
+void rank_table(const uint64_t *counts, int alphabet, uint8_t *rank_to_sym, uint8_t *sym_to_rank) {
+  std::vector<int> order(alphabet);
+  for (int i = 0; i < alphabet; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return counts[a] > counts[b]; });
+  for (int r = 0; r < alphabet; ++r) {
+    rank_to_sym[r] = (uint8_t)order[r];
+    sym_to_rank[order[r]] = (uint8_t)r;
+  }
+}
+
+// BF16 exponent/sign byte h = sign<<7 | symbol: rank r < 8 -> r ones, a zero,
+// the sign; otherwise 8 ones, the sign, the 7 symbol bits.
+void bf16_codes(const uint8_t *sym_to_rank, CodeTable &t) {
+  for (int h = 0; h < 256; ++h) {
+    const uint32_t s = h >> 7, e = h & 0x7F, r = sym_to_rank[e];
+    if (r < NWC_ESCAPE_R) {
+      t.val[h] = ((1u << r) - 1) | (s << (r + 1));
+      t.len[h] = (uint8_t)(r + 2);
+    } else {
+      t.val[h] = 0xFFu | (s << 8) | (e << 9);
+      t.len[h] = 16;
+    }
+  }
+}
+
+// fp8 byte b = sign<<7 | E<<3 | M: rank of E as unary, then sign and the 3
+// mantissa bits; escape: 8 ones, sign, E (4 bits), M (3 bits).
+void fp8_codes(const uint8_t *sym_to_rank, CodeTable &t) {
+  for (int b = 0; b < 256; ++b) {
+    const uint32_t s = b >> 7, E = (b >> 3) & 15, M = b & 7, r = sym_to_rank[E];
+    if (r < NWC_ESCAPE_R) {
+      t.val[b] = ((1u << r) - 1) | (s << (r + 1)) | (M << (r + 2));
+      t.len[b] = (uint8_t)(r + 5);
+    } else {
+      t.val[b] = 0xFFu | (s << 8) | (E << 9) | (M << 13);
+      t.len[b] = 16;
+    }
+  }
+}
+
+int trailing_ones(uint32_t v) { return v == 0xFFFFFFFFu ? 32 : __builtin_ctz(~v); }
+
+// BF16 bit pattern of an e4m3fn byte (exact: every e4m3fn value is a BF16 value).
+uint32_t fp8_to_bf16(uint32_t b) {
+  const uint32_t s = (b >> 7) & 1, E = (b >> 3) & 15, M = b & 7;
+  if (E == 15 && M == 7) return (s << 15) | 0x7FC0u;
+  if (E == 0) {
+    if (M == 0) return s << 15;
+    int p = 31 - __builtin_clz(M);                     // M * 2^-9 = 2^(p-9) * (M / 2^p)
+    return (s << 15) | ((uint32_t)(p + 118) << 7) | ((M ^ (1u << p)) << (7 - p));
+  }
+  return (s << 15) | ((E + 120) << 7) | (M << 4);
+}
+
+// Decode table for a 12-bit peek (layout in nwc_format.h).
+void build_lut_bf16(const uint8_t *rank_to_sym, uint32_t *lut) {
+  for (uint32_t p = 0; p < NWC_LUT_ENTRIES; ++p) {
+    uint32_t entry = 0x80000000u;
+    const int ra = trailing_ones(p);
+    if (ra < NWC_ESCAPE_R) {
+      const uint32_t la = ra + 2, sa = (p >> (ra + 1)) & 1;
+      const uint32_t q = p >> la, avail = 12 - la;
+      const int rb = trailing_ones(q);
+      if (rb < NWC_ESCAPE_R && (uint32_t)rb + 2 <= avail) {
+        const uint32_t lb = rb + 2, sb = (q >> (rb + 1)) & 1;
+        const uint32_t ha = (sa << 7) | rank_to_sym[ra], hb = (sb << 7) | rank_to_sym[rb];
+        entry = ha | (hb << 8) | ((la + lb) << 16);
+      }
+    }
+    lut[p] = entry;
+  }
+}
+
+void build_lut_fp8(const uint8_t *rank_to_sym, uint32_t *lut) {
+  for (uint32_t p = 0; p < NWC_LUT_ENTRIES; ++p) {
+    uint32_t entry = 0x80000000u;
+    const int r = trailing_ones(p);
+    if (r < NWC_ESCAPE_R) {  // r + 5 <= 12 bits: always complete
+      const uint32_t s = (p >> (r + 1)) & 1, M = (p >> (r + 2)) & 7, E = rank_to_sym[r];
+      const uint32_t b = (s << 7) | (E << 3) | M;
+      entry = fp8_to_bf16(b) | (b << 16) | ((uint32_t)(r + 5) << 24);
+    }
+    lut[p] = entry;
+  }
+}
+
+struct Plan {
+  int64_t n, k, ld;
+  int elem;
+  int C;
+  int64_t n_rb, n_ks, n_items;
+  std::vector<uint32_t> rows;  // code rows per item
+};
+
+inline uint32_t symbol_index(const void *w, int elem, int64_t idx) {
+  return elem == NWC_BF16 ? (uint32_t)(((const uint16_t *)w)[idx] >> 8) : (uint32_t)((const uint8_t *)w)[idx];
+}
+
+int auto_cols(int64_t n, int64_t k) {
+  const int64_t n_rb = nwc_ceil_div(n, NWC_LANES);
+  int C = NWC_MAX_COLS;
+  while (C > NWC_MIN_COLS && n_rb * nwc_ceil_div(k, C) < 2048) C /= 2;
+  return (int)std::min<int64_t>(C, nwc_round_up(k, 16));
+}
+
+// Longest lane stream (in 32-bit words) of every item for column count C.
+void plan_rows(const void *w, const CodeTable &tab, Plan &p) {
+  p.n_rb = nwc_ceil_div(p.n, NWC_LANES);
+  p.n_ks = nwc_ceil_div(p.k, p.C);
+  p.n_items = p.n_rb * p.n_ks;
+  p.rows.assign(p.n_items, 1);
+  parallel_for(p.n_rb, [&](int64_t b0, int64_t b1) {
+    for (int64_t rb = b0; rb < b1; ++rb)
+      for (int64_t ks = 0; ks < p.n_ks; ++ks) {
+        const int64_t c0 = ks * p.C, c1 = std::min<int64_t>(p.k, c0 + p.C);
+        uint64_t maxbits = NWC_LEAD_BITS;
+        for (int64_t L = 0; L < NWC_LANES; ++L) {
+          const int64_t row = rb * NWC_LANES + L;
+          if (row >= p.n) break;
+          uint64_t bits = NWC_LEAD_BITS;
+          const int64_t base = row * p.ld;
+          for (int64_t c = c0; c < c1; ++c) bits += tab.len[symbol_index(w, p.elem, base + c)];
+          maxbits = std::max(maxbits, bits);
+        }
+        p.rows[rb * p.n_ks + ks] = (uint32_t)nwc_ceil_div((int64_t)maxbits, 32);
+      }
+  });
+}
+
+int64_t bound_bytes(int64_t n, int64_t k, int elem) {
+  // Worst case over every admissible column count: 16 code bits per weight.
+  int64_t worst = 0;
+  for (int C = 16; C <= NWC_MAX_COLS; C += 16) {
+    const int64_t n_rb = nwc_ceil_div(n, NWC_LANES), n_ks = nwc_ceil_div(k, C);
+    const int64_t items = n_rb * n_ks;
+    const int64_t k_pad = (n_ks - 1) * C + nwc_round_up(k - (n_ks - 1) * C, 16);
+    const int64_t mant = elem == NWC_BF16 ? n_rb * NWC_LANES * k_pad : 0;
+    const int64_t rows = nwc_ceil_div(NWC_LEAD_BITS + 16 * (int64_t)C, 32);
+    const int64_t code = items * rows * 256;
+    worst = std::max(worst, NWC_HEADER_BYTES + NWC_LUT_BYTES + nwc_round_up(items * 8, 256) + mant + code);
+  }
+  return worst;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nwc_version(void) { return NWC_VERSION; }
+
+const char *nwc_status_string(int s) {
+  switch (s) {
+    case NWC_OK: return "ok";
+    case NWC_ERR_ARG: return "invalid argument (null or misaligned pointer, bad enum)";
+    case NWC_ERR_SHAPE: return "shape out of range";
+    case NWC_ERR_CAPACITY: return "buffer or workspace too small";
+    case NWC_ERR_FORMAT: return "not a valid blob of this format version";
+    case NWC_ERR_HIP: return "HIP runtime error";
+    case NWC_ERR_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_item, int64_t *max_bytes) {
+  if (!max_bytes) return NWC_ERR_ARG;
+  if (elem != NWC_BF16 && elem != NWC_FP8_E4M3) return NWC_ERR_ARG;
+  if (cols_per_item != 0 && (cols_per_item < 16 || cols_per_item > NWC_MAX_COLS || cols_per_item % 16))
+    return NWC_ERR_ARG;
+  if (n <= 0 || k <= 0 || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return NWC_ERR_SHAPE;
+  *max_bytes = bound_bytes(n, k, elem);
+  return NWC_OK;
+}
+
+int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_item, void *blob,
+               int64_t blob_cap, int64_t *blob_size) {
+  if (!w || !blob || !blob_size) return NWC_ERR_ARG;
+  if (elem != NWC_BF16 && elem != NWC_FP8_E4M3) return NWC_ERR_ARG;
+  if (cols_per_item != 0 && (cols_per_item < 16 || cols_per_item > NWC_MAX_COLS || cols_per_item % 16))
+    return NWC_ERR_ARG;
+  if (n <= 0 || k <= 0 || ld < k || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return NWC_ERR_SHAPE;
+
+  // 1. histogram of the ranked symbol over the real weights
+  const int alphabet = elem == NWC_BF16 ? 128 : 16;
+  std::vector<uint64_t> counts(alphabet, 0);
+  {
+    const int t = worker_count();
+    std::vector<std::vector<uint64_t>> part(t, std::vector<uint64_t>(alphabet, 0));
+    std::vector<std::thread> th;
+    for (int i = 0; i < t; ++i)
+      th.emplace_back([&, i] {
+        auto &h = part[i];
+        for (int64_t r = n * i / t; r < n * (i + 1) / t; ++r) {
+          if (elem == NWC_BF16) {
+            const uint16_t *row = (const uint16_t *)w + r * ld;
+            for (int64_t c = 0; c < k; ++c) h[(row[c] >> 8) & 0x7F]++;
+          } else {
+            const uint8_t *row = (const uint8_t *)w + r * ld;
+            for (int64_t c = 0; c < k; ++c) h[(row[c] >> 3) & 15]++;
+          }
+        }
+      });
+    for (auto &x : th) x.join();
+    for (auto &h : part)
+      for (int s = 0; s < alphabet; ++s) counts[s] += h[s];
+  }
+
+  // 2. rank table and codewords
+  nwc_header_t hd;
+  memset(&hd, 0, sizeof hd);
+  uint8_t sym_to_rank[128] = {0};
+  rank_table(counts.data(), alphabet, hd.rank_to_sym, sym_to_rank);
+  CodeTable tab;
+  if (elem == NWC_BF16)
+    bf16_codes(sym_to_rank, tab);
+  else
+    fp8_codes(sym_to_rank, tab);
+
+  // 3. work-item geometry; shrink the column span if a stream would not fit
+  Plan p{n, k, ld, elem, cols_per_item ? cols_per_item : auto_cols(n, k), 0, 0, 0, {}};
+  p.C = (int)std::min<int64_t>(p.C, nwc_round_up(k, 16));
+  for (;;) {
+    plan_rows(w, tab, p);
+    const uint32_t mx = *std::max_element(p.rows.begin(), p.rows.end());
+    if (mx <= NWC_ROWS_CAP) break;
+    if (p.C <= NWC_MIN_COLS) return NWC_ERR_UNSUPPORTED;  // cannot happen: 64 cols need <= 33 rows
+    p.C = std::max(NWC_MIN_COLS, p.C / 2);
+  }
+
+  // 4. layout
+  hd.magic = NWC_MAGIC;
+  hd.version = NWC_FORMAT_VERSION;
+  hd.elem = (uint32_t)elem;
+  hd.header_bytes = NWC_HEADER_BYTES;
+  hd.n = n;
+  hd.k = k;
+  hd.cols_per_item = (uint32_t)p.C;
+  hd.n_rowblocks = (uint32_t)p.n_rb;
+  hd.n_kspans = (uint32_t)p.n_ks;
+  hd.n_items = (uint32_t)p.n_items;
+  hd.max_rows = *std::max_element(p.rows.begin(), p.rows.end());
+  hd.escape_r = NWC_ESCAPE_R;
+  hd.last_cols = (uint32_t)(k - (p.n_ks - 1) * p.C);
+  hd.k_pad = (uint32_t)((p.n_ks - 1) * p.C + nwc_round_up(hd.last_cols, 16));
+  hd.off_lut = NWC_HEADER_BYTES;
+  hd.off_items = hd.off_lut + NWC_LUT_BYTES;
+  hd.off_mant = hd.off_items + (uint64_t)nwc_round_up(p.n_items * 8, 256);
+  hd.mant_bytes = elem == NWC_BF16 ? (uint64_t)p.n_rb * NWC_LANES * hd.k_pad : 0;
+  hd.off_code = hd.off_mant + hd.mant_bytes;
+  std::vector<uint32_t> code_off(p.n_items);
+  uint64_t code_bytes = 0;
+  for (int64_t i = 0; i < p.n_items; ++i) {
+    code_off[i] = (uint32_t)code_bytes;
+    code_bytes += (uint64_t)p.rows[i] * 256;
+  }
+  if (code_bytes > 0xFFFFFFFFull) return NWC_ERR_SHAPE;  // item offsets are 32-bit
+  hd.code_bytes = code_bytes;
+  hd.total_bytes = hd.off_code + code_bytes;
+  if ((int64_t)hd.total_bytes > blob_cap) return NWC_ERR_CAPACITY;
+
+  // 5. coded size of the real weights (sum of codeword lengths + raw bytes)
+  // (codeword length depends on the rank only, not on sign or fp8 mantissa)
+  uint64_t coded = 0;
+  for (int s = 0; s < alphabet; ++s) coded += counts[s] * tab.len[elem == NWC_BF16 ? s : (s << 3)];
+  if (elem == NWC_BF16) coded += 8ull * (uint64_t)n * (uint64_t)k;
+  hd.coded_bits = coded;
+
+  // 6. write header, decode table, item table
+  uint8_t *out = (uint8_t *)blob;
+  memset(out, 0, hd.off_code);
+  memcpy(out, &hd, sizeof hd);
+  uint32_t *lut = (uint32_t *)(out + hd.off_lut);
+  if (elem == NWC_BF16)
+    build_lut_bf16(hd.rank_to_sym, lut);
+  else
+    build_lut_fp8(hd.rank_to_sym, lut);
+  uint32_t *items = (uint32_t *)(out + hd.off_items);
+  for (int64_t i = 0; i < p.n_items; ++i) {
+    items[2 * i] = code_off[i];
+    items[2 * i + 1] = p.rows[i];
+  }
+
+  // 7. code and mantissa planes, one row block per task
+  parallel_for(p.n_rb, [&](int64_t b0, int64_t b1) {
+    for (int64_t rb = b0; rb < b1; ++rb)
+      for (int64_t ks = 0; ks < p.n_ks; ++ks) {
+        const int64_t item = rb * p.n_ks + ks;
+        const uint32_t rows = p.rows[item];
+        uint32_t *code = (uint32_t *)(out + hd.off_code + code_off[item]);
+        memset(code, 0, (size_t)rows * 256);
+        const int64_t c0 = ks * p.C, c1 = std::min<int64_t>(k, c0 + p.C), nc = c1 - c0;
+        uint8_t *mant = nullptr;
+        if (elem == NWC_BF16) {
+          mant = out + hd.off_mant + (uint64_t)rb * NWC_LANES * hd.k_pad + (uint64_t)NWC_LANES * c0;
+          memset(mant, 0, (size_t)NWC_LANES * nwc_round_up(nc, 16));
+        }
+        for (int64_t L = 0; L < NWC_LANES; ++L) {
+          const int64_t row = rb * NWC_LANES + L;
+          if (row >= n) break;
+          uint64_t acc = 0;
+          uint32_t nbits = NWC_LEAD_BITS, word = 0;
+          for (int64_t c = 0; c < nc; ++c) {
+            const int64_t idx = row * ld + c0 + c;
+            const uint32_t sym = symbol_index(w, elem, idx);
+            acc |= (uint64_t)tab.val[sym] << nbits;
+            nbits += tab.len[sym];
+            if (nbits >= 32) {
+              code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
+              acc >>= 32;
+              nbits -= 32;
+              ++word;
+            }
+            if (mant) mant[((c >> 4) * NWC_LANES + L) * 16 + (c & 15)] = (uint8_t)((const uint16_t *)w)[idx];
+          }
+          if (nbits) code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
+        }
+      }
+  });
+  *blob_size = (int64_t)hd.total_bytes;
+  return NWC_OK;
+}
+
+int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info) {
+  if (!blob || !info) return NWC_ERR_ARG;
+  if (blob_bytes < NWC_HEADER_BYTES) return NWC_ERR_CAPACITY;
+  nwc_header_t h;
+  memcpy(&h, blob, sizeof h);
+  const int st = nwc_check_header(&h);
+  if (st != NWC_OK) return st;
+  memset(info, 0, sizeof *info);
+  info->n = h.n;
+  info->k = h.k;
+  info->elem = (int32_t)h.elem;
+  info->cols_per_item = (int32_t)h.cols_per_item;
+  info->n_items = (int32_t)h.n_items;
+  info->max_rows = (int32_t)h.max_rows;
+  info->coded_bits = h.coded_bits;
+  info->total_bytes = h.total_bytes;
+  info->code_bytes = h.code_bytes;
+  info->mant_bytes = h.mant_bytes;
+  info->table_bytes = h.off_mant;
+  memcpy(info->rank_to_sym, h.rank_to_sym, 128);
+  return NWC_OK;
+}
+
+int nwc_workspace_size(const void *header, int64_t *bytes) {
+  if (!header || !bytes) return NWC_ERR_ARG;
+  nwc_header_t h;
+  memcpy(&h, header, sizeof h);
+  const int st = nwc_check_header(&h);
+  if (st != NWC_OK) return st;
+  if (h.n_kspans == 1) {
+    *bytes = 0;
+    return NWC_OK;
+  }
+  *bytes = nwc_round_up((int64_t)h.n_items * NWC_LANES * 4, 256) + nwc_round_up((int64_t)h.n_rowblocks * 4, 256);
+  return NWC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+"""Thin Python binding of libnwc (argument marshalling only).
+
+Every step of the hot path runs in the HIP library; this module only converts
+numpy arrays and torch tensors to pointers and sizes, and raises on error
+statuses.  torch is used for device memory and streams.  Importing this
+module fails loudly if the built library is missing: there is no fallback.
+
+Function names mirror the C ABI in include/nwc.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnwc.so")
+
+NWC_BF16 = 0
+NWC_FP8_E4M3 = 1
+HEADER_BYTES = 256
+
+STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPACITY",
+          -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
+
+EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info",
+           "nwc_workspace_size", "nwc_matvec", "nwc_dequant", "nwc_gather")
+
+
+class NWCError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class NWCInfo(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("elem", ctypes.c_int32),
+                ("cols_per_item", ctypes.c_int32), ("n_items", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+                ("coded_bits", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+                ("code_bytes", ctypes.c_uint64), ("mant_bytes", ctypes.c_uint64),
+                ("table_bytes", ctypes.c_uint64), ("rank_to_sym", ctypes.c_uint8 * 128)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libnwc.so not built ({LIB_PATH}); run `python -m decode_matvec_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    sig = {
+        "nwc_version": ([], ci),
+        "nwc_status_string": ([ci], ctypes.c_char_p),
+        "nwc_encode_bound": ([i64, i64, ci, ci, ctypes.POINTER(i64)], ci),
+        "nwc_encode": ([vp, i64, i64, i64, ci, ci, vp, i64, ctypes.POINTER(i64)], ci),
+        "nwc_blob_info": ([vp, i64, ctypes.POINTER(NWCInfo)], ci),
+        "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
+        "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
+        "nwc_dequant": ([vp, vp, vp, i64, vp], ci),
+        "nwc_gather": ([vp, vp, vp, i64, vp, vp], ci),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise NWCError(fn, st, lib.nwc_status_string(st).decode())
+
+
+def version() -> int:
+    return lib.nwc_version()
+
+
+def status_string(st: int) -> str:
+    return lib.nwc_status_string(st).decode()
+
+
+def _host_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def encode_bound(n: int, k: int, elem: int = NWC_BF16, cols_per_item: int = 0) -> int:
+    out = ctypes.c_int64()
+    _check("nwc_encode_bound", lib.nwc_encode_bound(n, k, elem, cols_per_item, ctypes.byref(out)))
+    return out.value
+
+
+def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_item: int = 0) -> np.ndarray:
+    """Encode a host matrix (uint16 BF16 patterns or uint8 fp8 bytes) -> uint8 blob."""
+    want = np.uint16 if elem == NWC_BF16 else np.uint8
+    if w.dtype != want or w.ndim != 2:
+        raise TypeError(f"expected a 2-D {np.dtype(want).name} array, got {w.dtype} {w.shape}")
+    if w.strides[1] != w.itemsize:
+        w = np.ascontiguousarray(w)
+    n, k = w.shape
+    ld = w.strides[0] // w.itemsize
+    cap = encode_bound(n, k, elem, cols_per_item)
+    blob = np.empty(cap, dtype=np.uint8)
+    size = ctypes.c_int64()
+    _check("nwc_encode", lib.nwc_encode(_host_ptr(w), n, k, ld, elem, cols_per_item, _host_ptr(blob), cap,
+                                        ctypes.byref(size)))
+    return blob[:size.value].copy()
+
+
+def blob_info(blob: np.ndarray) -> dict:
+    info = NWCInfo()
+    _check("nwc_blob_info", lib.nwc_blob_info(_host_ptr(blob), blob.nbytes, ctypes.byref(info)))
+    d = {f: getattr(info, f) for f, _ in NWCInfo._fields_ if f != "rank_to_sym"}
+    d["rank_to_sym"] = list(info.rank_to_sym)
+    return d
+
+
+def workspace_size(header: np.ndarray) -> int:
+    out = ctypes.c_int64()
+    _check("nwc_workspace_size", lib.nwc_workspace_size(_host_ptr(header), ctypes.byref(out)))
+    return out.value
+
+
+def _dev(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def matvec(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -> None:
+    """y[n] (fp32) = W x (times scale for fp8) on the GPU; all device arguments are torch tensors."""
+    _check("nwc_matvec", lib.nwc_matvec(_host_ptr(header), _dev(d_blob), _dev(x), _dev(scale), _dev(y), _dev(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dequant(header: np.ndarray, d_blob, out, ld: int, stream=None) -> None:
+    _check("nwc_dequant", lib.nwc_dequant(_host_ptr(header), _dev(d_blob), _dev(out), ld, _stream(stream)))
+
+
+def gather(header: np.ndarray, d_blob, ids, out, stream=None) -> None:
+    _check("nwc_gather", lib.nwc_gather(_host_ptr(header), _dev(d_blob), _dev(ids), ids.numel(), _dev(out),
+                                        _stream(stream)))
+
+
+class DeviceMatrix:
+    """A compressed matrix resident on the GPU: host header copy + device blob + workspace.
+
+    Holds buffers only; every computation is a call into libnwc."""
+
+    def __init__(self, blob: np.ndarray, device="cuda"):
+        import torch
+        self.info = blob_info(blob)
+        self.header = np.ascontiguousarray(blob[:HEADER_BYTES]).copy()
+        self.d_blob = torch.from_numpy(blob).to(device)
+        wsb = workspace_size(self.header)
+        self.ws = torch.zeros(max(wsb, 0) // 4, dtype=torch.int32, device=device) if wsb else None
+        self.n, self.k = self.info["n"], self.info["k"]
+        self.elem = self.info["elem"]
+        self.nbytes = int(blob.nbytes)
+
+    def matvec(self, x, y, scale=None, stream=None):
+        matvec(self.header, self.d_blob, x, y, self.ws, scale, stream)
+
+    def dequant(self, out, ld=None, stream=None):
+        dequant(self.header, self.d_blob, out, self.k if ld is None else ld, stream)
+
+    def gather(self, ids, out, stream=None):
+        gather(self.header, self.d_blob, ids, out, stream)

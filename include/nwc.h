@@ -1,0 +1,133 @@
+/*
+ * nwc.h -- C ABI of libnwc: batch-1 matrix-vector products over losslessly
+ * compressed BF16 (and fp8 e4m3) weights on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the "neural-weight-compression 0.9.0"
+ * PyPI page: the library holds "encoder, fused matvec, dequantization, gather"
+ * ("Repository layout"); weights stay compressed and are decoded in registers
+ * inside the matvec ("How it works", "Fused kernel"); dequantization and the
+ * embedding lookup run on the same decoder.  The fp8 variant follows the
+ * "Qwen3-4B-NWC-fp8" model card (weight-only e4m3, per-output-channel scale
+ * applied at the end of the row sum, fp8 bytes recovered bit for bit).
+ *
+ * Conventions for every entry point:
+ *  - Return value: NWC_OK (0) or a negative nwc_status.  Nothing aborts,
+ *    throws, prints, allocates device memory or synchronizes the device.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check enqueues nothing.  Faults inside kernels (for example a device
+ *    pointer that does not hold the blob it claims to) surface at the caller's
+ *    next synchronization, not here.
+ *  - "header" is a HOST pointer to the first NWC_HEADER_BYTES bytes of the
+ *    blob (the caller keeps a host copy of the header; launches never read
+ *    device memory on the host).  "d_blob" is the same blob in device memory.
+ *  - Device work is enqueued on `stream`, a hipStream_t (NULL = the legacy
+ *    default stream).  The caller owns every buffer.
+ *  - Matrices are row-major: W has n rows (outputs) and k columns (inputs).
+ */
+#ifndef NWC_H
+#define NWC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NWC_VERSION 10000 /* 1.0.0 */
+#define NWC_HEADER_BYTES 256
+
+typedef enum nwc_status {
+  NWC_OK = 0,
+  NWC_ERR_ARG = -1,         /* null/misaligned pointer, bad enum or flag */
+  NWC_ERR_SHAPE = -2,       /* n, k, ld or a count out of range */
+  NWC_ERR_CAPACITY = -3,    /* caller's buffer or workspace too small */
+  NWC_ERR_FORMAT = -4,      /* header is not a valid blob of this version */
+  NWC_ERR_HIP = -5,         /* the HIP runtime refused a launch */
+  NWC_ERR_UNSUPPORTED = -6  /* valid request this build does not serve */
+} nwc_status;
+
+typedef enum nwc_elem {
+  NWC_BF16 = 0,     /* input: uint16 BF16 bit patterns */
+  NWC_FP8_E4M3 = 1  /* input: uint8 e4m3fn bytes (already quantized) */
+} nwc_elem;
+
+/* Blob metadata, filled by nwc_blob_info. */
+typedef struct nwc_info {
+  int64_t n, k;
+  int32_t elem;
+  int32_t cols_per_item;   /* columns per work item (per-lane stream length) */
+  int32_t n_items;         /* 64-row x cols_per_item work items */
+  int32_t max_rows;        /* longest item code column, in 32-bit words */
+  uint64_t coded_bits;     /* sum of codeword lengths of the real weights, plus
+                              8 raw mantissa bits per BF16 weight */
+  uint64_t total_bytes;    /* whole blob */
+  uint64_t code_bytes;     /* code plane incl. per-item zero padding */
+  uint64_t mant_bytes;     /* mantissa plane (0 for fp8) */
+  uint64_t table_bytes;    /* header + decode table + item table */
+  uint8_t rank_to_sym[128];/* frequency rank -> symbol (16 used for fp8) */
+} nwc_info;
+
+/* Library version (NWC_VERSION of the build). */
+int nwc_version(void);
+
+/* Static description of a status code. */
+const char *nwc_status_string(int status);
+
+/* Upper bound of the blob size nwc_encode can produce for an n x k matrix.
+ * cols_per_item: 0 (automatic) or a multiple of 16 in [64, 256]. */
+int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_item, int64_t *max_bytes);
+
+/* Host-side encoder ("How it works": byte planes, per-matrix frequency rank
+ * table, unary rank code + raw sign + escape; model card: fp8 bytes coded whole).
+ *   w_host   n rows of k elements, row pitch ld elements (ld >= k); uint16 BF16
+ *            patterns for NWC_BF16, uint8 e4m3fn bytes for NWC_FP8_E4M3.
+ *   blob     caller-owned host buffer of blob_cap bytes (see nwc_encode_bound);
+ *            on success the blob occupies *blob_size bytes from its start.
+ *   cols_per_item: 0 = choose from the shape; else a multiple of 16 in
+ *            [64, 256] (reduced automatically if a work item's longest code
+ *            column would exceed the decoder's staging capacity).
+ * Any BF16 pattern (NaN payloads, infinities, zeros, subnormals) and any fp8
+ * byte is encoded losslessly.  Uses up to hardware_concurrency host threads. */
+int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_item,
+               void *blob, int64_t blob_cap, int64_t *blob_size);
+
+/* Validate a blob header (host pointer, at least NWC_HEADER_BYTES) and
+ * describe it.  blob_bytes: bytes available at `blob` (>= header bytes). */
+int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info);
+
+/* Device workspace bytes nwc_matvec needs for this blob (0 if the matrix has
+ * a single column span).  Layout: fp32 partial sums, then one 32-bit counter
+ * per 64-row block.  The counters must be zero before the first call (for
+ * example a zero-filled allocation); every call leaves them zero again. */
+int nwc_workspace_size(const void *header, int64_t *bytes);
+
+/* Fused decode + matvec ("Fused kernel": weights decoded in registers, fp32
+ * row sums; model card: fp8 scale applied after the row sum).
+ *   d_x      device, k BF16 patterns (uint16), 16-byte aligned.
+ *   d_scale  device, n fp32 scales for NWC_FP8_E4M3 blobs; must be NULL for BF16.
+ *   d_y      device, n fp32 outputs, 4-byte aligned:  y_i = (s_i *) sum_j w_ij x_j.
+ *   d_ws     device workspace of ws_bytes >= nwc_workspace_size, 256-byte
+ *            aligned; may be NULL when the size is 0.  Concurrent calls need
+ *            distinct workspaces.
+ * The summation order is fixed, so repeated calls give identical bits. */
+int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const float *d_scale,
+               float *d_y, void *d_ws, int64_t ws_bytes, void *stream);
+
+/* Dequantization to the stored element type ("How it works": dequantization
+ * runs on the same decoder).  BF16 blobs write uint16 BF16 patterns, fp8 blobs
+ * write the fp8 bytes (the scale is not applied).  Row i of the matrix goes to
+ * d_w + i*ld elements (ld >= k); d_w 16-byte aligned. Bit-exact. */
+int nwc_dequant(const void *header, const void *d_blob, void *d_w, int64_t ld, void *stream);
+
+/* Embedding lookup on the same decoder ("How it works": tied lm_head and
+ * embedding share one encoding).  For t < n_ids, row d_ids[t] is decoded to
+ * d_out + t*k elements (BF16 patterns or fp8 bytes).  Ids outside [0, n)
+ * produce a zero row.  d_ids: device int64; bit-exact. */
+int nwc_gather(const void *header, const void *d_blob, const int64_t *d_ids, int64_t n_ids,
+               void *d_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NWC_H */

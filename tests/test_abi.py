@@ -1,0 +1,194 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+checks its arguments before touching the GPU, and its host encoder agrees with
+the oracle (rank table, coded size, layout, decode table).  No GPU needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth as S
+from synth import configs as C
+from decode_matvec_amd import nwc
+
+from . import blob_layout as BL
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "nwc.h")).read()
+    declared = set(re.findall(r"^(?:int|const char \*)\s*(nwc_\w+)\s*\(", hdr, re.M))
+    assert declared == set(nwc.EXPORTS)
+    lib = ctypes.CDLL(nwc.LIB_PATH)
+    for name in declared:
+        assert getattr(lib, name) is not None
+    assert nwc.version() == 10000
+    assert nwc.status_string(0) == "ok"
+    assert "format" in nwc.status_string(-4)
+
+
+def _mats():
+    out = [("single", S.normal_bf16(1, (1024, 1024), 0.02)),
+           ("all_patterns", S.all_patterns_bf16())]
+    for idx, (n, k) in enumerate(C.ODD_SHAPES):
+        out.append((f"odd{n}x{k}", S.inject_rare(S.student_t_bf16(C.odd_seed(2 * idx + 1), (n, k)),
+                                                   C.odd_seed(2 * idx + 1) + 50)))
+    return out
+
+
+@pytest.mark.parametrize("name,w", _mats(), ids=lambda v: v if isinstance(v, str) else "")
+def test_encoder_matches_oracle_rank_and_size(name, w):
+    blob = nwc.encode(w)
+    info = nwc.blob_info(blob)
+    enc = O.encode_bf16(w)
+    assert info["rank_to_sym"] == [int(v) for v in enc["rank_to_sym"]]
+    assert info["coded_bits"] == enc["coded_bits"]
+    assert info["n"], info["k"] == w.shape
+
+
+def test_encoder_fp8_matches_oracle():
+    q, _ = S.fp8_quantize(S.normal_bf16(1, (1024, 1024), 0.02))
+    for m in (q, S.all_bytes_fp8(3)):
+        blob = nwc.encode(m, elem=nwc.NWC_FP8_E4M3)
+        info = nwc.blob_info(blob)
+        enc = O.encode_fp8(m)
+        assert info["rank_to_sym"][:16] == [int(v) for v in enc["rank_to_sym"]]
+        assert info["coded_bits"] == enc["coded_bits"]
+
+
+@pytest.mark.parametrize("shape,cols,seed", [((70, 333), 64, 1), ((130, 100), 0, 2), ((3, 600), 256, 3),
+                                             ((64, 48), 16, 4)])
+def test_blob_layout_decodes_to_input(shape, cols, seed):
+    w = S.inject_rare(S.student_t_bf16(seed, shape), seed + 7, frac=0.02)
+    blob = nwc.encode(w, cols_per_item=cols)
+    assert np.array_equal(BL.decode_blob(blob), w)
+    q, _ = S.fp8_quantize(w)
+    blob8 = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_item=cols)
+    assert np.array_equal(BL.decode_blob(blob8), q)
+
+
+def test_all_patterns_blob_layout():
+    w = S.all_patterns_bf16()
+    assert np.array_equal(BL.decode_blob(nwc.encode(w)), w)
+
+
+def test_decode_table_bf16_against_oracle():
+    w = S.normal_bf16(9, (300, 500), 0.02)
+    blob = nwc.encode(w)
+    r2s = np.array(BL.header(blob)["rank_to_sym"], dtype=np.int64)
+    lut = BL.lut(blob)
+    for p in range(4096):
+        bits = [(p >> i) & 1 for i in range(12)]
+        e = int(lut[p])
+        # Oracle parse of the two leading codes, if both end inside the 12 bits.
+        pad = bits + [0] * 32
+        sa, ea, pa = O.parse_one_bf16(pad, 0, r2s)
+        ok = pa <= 12 and sum(bits[:8]) < 8 or False
+        if ok and not (pa == 16):
+            sb, eb, pb = O.parse_one_bf16(pad, pa, r2s)
+            ok = pb <= 12 and pb - pa != 16
+        if ok:
+            assert e == ((sa << 7) | ea) | (((sb << 7) | eb) << 8) | (pb << 16), p
+        else:
+            assert e == 0x80000000, p
+
+
+def test_decode_table_fp8_against_oracle():
+    q, _ = S.fp8_quantize(S.normal_bf16(1, (256, 256), 0.02))
+    blob = nwc.encode(q, elem=nwc.NWC_FP8_E4M3)
+    lut = BL.lut(blob)
+    h = BL.header(blob)
+    import torch
+    for p in range(4096):
+        e = int(lut[p])
+        bits = [(p >> i) & 1 for i in range(12)]
+        if all(bits[:8]):
+            assert e == 0x80000000
+            continue
+        r = bits.index(0)
+        s = bits[r + 1]
+        M = bits[r + 2] | bits[r + 3] << 1 | bits[r + 4] << 2
+        E = h["rank_to_sym"][r]
+        b = (s << 7) | (E << 3) | M
+        bf = torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.bfloat16)
+        want = int(bf.view(torch.int16).item()) & 0xFFFF
+        if torch.isnan(bf).item():   # torch canonicalises the NaN sign; any BF16 NaN will do
+            assert (e & 0x7F80) == 0x7F80 and (e & 0x7F) != 0
+        else:
+            assert e & 0xFFFF == want
+        assert (e >> 16) & 0xFF == b and (e >> 24) == r + 5
+
+
+def test_encoder_argument_errors():
+    w = np.zeros((4, 8), np.uint16)
+    blob = np.zeros(1 << 20, np.uint8)
+    size = ctypes.c_int64()
+    L = nwc.lib
+    assert L.nwc_encode(None, 4, 8, 8, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -1
+    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 7, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -1
+    assert L.nwc_encode(w.ctypes.data, 4, 8, 4, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -2
+    assert L.nwc_encode(w.ctypes.data, 0, 8, 8, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -2
+    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 24, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -1
+    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 0, blob.ctypes.data, 100, ctypes.byref(size)) == -3
+    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == 0
+    with pytest.raises(TypeError):
+        nwc.encode(w.astype(np.float32))
+
+
+def test_bound_covers_worst_case():
+    # The all-escape matrix (every symbol ties) is the longest code there is.
+    w = S.all_patterns_bf16()
+    assert nwc.encode(w).nbytes <= nwc.encode_bound(256, 256)
+    for cols in (16, 64, 256):
+        assert nwc.encode(w, cols_per_item=cols).nbytes <= nwc.encode_bound(256, 256, 0, cols)
+
+
+def test_header_validation_and_workspace():
+    w = S.normal_bf16(3, (200, 700), 0.02)
+    blob = nwc.encode(w, cols_per_item=128)
+    hdr = blob[:256].copy()
+    ws = nwc.workspace_size(hdr)
+    info = nwc.blob_info(blob)
+    n_rb = (200 + 63) // 64
+    assert ws == ((info["n_items"] * 64 * 4 + 255) // 256) * 256 + 256
+    assert info["n_items"] == n_rb * ((700 + 127) // 128)
+    bad = hdr.copy()
+    bad[0] ^= 1
+    with pytest.raises(nwc.NWCError) as ei:
+        nwc.workspace_size(bad)
+    assert ei.value.status == -4
+    bad = hdr.copy()
+    bad[8] = 5  # elem
+    with pytest.raises(nwc.NWCError):
+        nwc.blob_info(np.concatenate([bad, blob[256:]]))
+    # A single column span needs no workspace.
+    assert nwc.workspace_size(nwc.encode(S.normal_bf16(3, (70, 100), 0.02), cols_per_item=128)[:256].copy()) == 0
+
+
+def test_launchers_reject_bad_arguments_before_any_gpu_call():
+    w = S.normal_bf16(3, (200, 700), 0.02)
+    blob = nwc.encode(w, cols_per_item=128)
+    hdr = blob[:256].copy()
+    L = nwc.lib
+    fake = 1 << 20  # never dereferenced: every call below fails its host-side checks
+    ws = nwc.workspace_size(hdr)
+    assert L.nwc_matvec(None, fake, fake, None, fake, fake, ws, None) == -1
+    assert L.nwc_matvec(hdr.ctypes.data, 0, fake, None, fake, fake, ws, None) == -1
+    assert L.nwc_matvec(hdr.ctypes.data, fake + 4, fake, None, fake, fake, ws, None) == -1
+    assert L.nwc_matvec(hdr.ctypes.data, fake, fake, fake, fake, fake, ws, None) == -1   # BF16 with a scale
+    assert L.nwc_matvec(hdr.ctypes.data, fake, fake, None, fake, None, ws, None) == -1   # workspace missing
+    assert L.nwc_matvec(hdr.ctypes.data, fake, fake, None, fake, fake, ws - 4, None) == -3
+    bad = hdr.copy()
+    bad[4] = 9  # version
+    assert L.nwc_matvec(bad.ctypes.data, fake, fake, None, fake, fake, ws, None) == -4
+    assert L.nwc_dequant(hdr.ctypes.data, fake, fake, 699, None) == -2
+    assert L.nwc_dequant(hdr.ctypes.data, fake, fake + 2, 700, None) == -1
+    assert L.nwc_gather(hdr.ctypes.data, fake, fake, -1, fake, None) == -2
+    assert L.nwc_gather(hdr.ctypes.data, fake, fake + 4, 5, fake, None) == -1
+    assert L.nwc_gather(hdr.ctypes.data, fake, fake, 0, fake, None) == 0   # nothing to do
+    q, _ = S.fp8_quantize(w)
+    h8 = nwc.encode(q, elem=1, cols_per_item=128)[:256].copy()
+    assert L.nwc_matvec(h8.ctypes.data, fake, fake, None, fake, fake, ws, None) == -1   # fp8 needs a scale

@@ -1,0 +1,218 @@
+"""GPU parity of libnwc against the CPU oracle, through the C ABI.
+
+Decode (dequant) and gather must be bit-exact; the matvec must satisfy
+|y - y_ref| <= 1e-3 * sum_j |w_ij x_j| + 1e-6 per output, y_ref the oracle's
+float64 sum.  Small workloads are checked element by element; the full-size
+workloads are checked on every dequantized element (against the oracle's
+lossless decode, which is the input) and on sampled matvec outputs that the
+oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth as S
+from synth import configs as C
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from decode_matvec_amd import nwc  # noqa: E402
+
+DEV = "cuda"
+RTOL, ATOL = 1e-3, 1e-6
+
+
+def dev16(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+def host16(t) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_matvec(dm, x_u16, scale=None):
+    y = torch.full((dm.n,), float("nan"), dtype=torch.float32, device=DEV)
+    dm.matvec(dev16(x_u16), y, scale=None if scale is None else torch.from_numpy(scale).to(DEV))
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def check_tol(y, y_ref, A, what=""):
+    err = np.abs(y - y_ref)
+    bad = ~(err <= RTOL * A + ATOL)
+    assert not bad.any(), f"{what}: {bad.sum()} outputs out of tolerance, worst row {np.argmax(err - RTOL * A)}"
+
+
+def dequant_host(dm, ld=None):
+    ld = dm.k if ld is None else ld
+    dt = torch.int16 if dm.elem == 0 else torch.uint8
+    out = torch.full((dm.n, ld), -1, dtype=dt, device=DEV)
+    dm.dequant(out, ld=ld)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    return (o.view(np.uint16) if dm.elem == 0 else o)[:, :dm.k]
+
+
+def full_parity_bf16(w, x, cols=0, check_matvec=True):
+    print(f"case shape={w.shape} cols={cols}", flush=True)
+    dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_item=cols), DEV)
+    enc = O.encode_bf16(w)
+    assert np.array_equal(dequant_host(dm), O.decode_bf16(enc))
+    if check_matvec:
+        y_ref, A = O.matvec_bf16_ref(w, x)
+        y = run_matvec(dm, x)
+        check_tol(y, y_ref, A, f"{w.shape}")
+        y2 = run_matvec(dm, x)
+        assert np.array_equal(y, y2), "matvec not deterministic"
+    return dm
+
+
+# ----------------------------------------------------------------- single 1024 x 1024
+@pytest.mark.parametrize("cols", [0, 16, 64, 128, 256])
+def test_single_matrix(cols):
+    w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
+    x = S.activation_bf16(C.SINGLE["x_seed"], 1024)
+    full_parity_bf16(w, x, cols)
+
+
+def test_dequant_row_pitch():
+    w = S.normal_bf16(5, (130, 200), 0.02)
+    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
+    assert np.array_equal(dequant_host(dm, ld=216), w)
+
+
+# ----------------------------------------------------------------- odd shapes, rare values
+def _odd_cases():
+    out = []
+    for idx, (n, k) in enumerate(C.ODD_SHAPES):
+        for kind in ("normal", "t3"):
+            out.append((idx, n, k, kind))
+    return out
+
+
+@pytest.mark.parametrize("idx,n,k,kind", _odd_cases())
+def test_odd_shapes(idx, n, k, kind):
+    seed = C.odd_seed(2 * idx + (kind == "t3"))
+    w = S.normal_bf16(seed, (n, k), 0.02) if kind == "normal" else S.student_t_bf16(seed, (n, k))
+    w = S.inject_rare(w, seed + 50)
+    x = S.activation_bf16(seed + 60, k)
+    full_parity_bf16(w, x)
+
+
+def test_all_patterns_dequant_and_gather():
+    w = S.all_patterns_bf16()
+    dm = full_parity_bf16(w, None, check_matvec=False)
+    ids = np.array([0, 255, 127, 128, 128, -3, 256, 1000, 7], dtype=np.int64)
+    out = torch.full((len(ids), 256), -1, dtype=torch.int16, device=DEV)
+    dm.gather(torch.from_numpy(ids).to(DEV), out)
+    torch.cuda.synchronize()
+    enc = O.encode_bf16(w)
+    assert np.array_equal(host16(out), O.gather_bf16_ref(enc, ids))
+
+
+# ----------------------------------------------------------------- exact special cases
+def test_exact_special_cases():
+    w = S.normal_bf16(31, (200, 300), 0.02)
+    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
+    for j in (0, 150, 299):
+        x = np.zeros(300, np.uint16)
+        x[j] = 0x3F80
+        y_ref, _ = O.matvec_bf16_ref(w, x)
+        assert np.array_equal(run_matvec(dm, x), y_ref)
+    eye = np.where(np.eye(256, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    x = S.activation_bf16(32, 256)
+    dm = nwc.DeviceMatrix(nwc.encode(eye), DEV)
+    assert np.array_equal(run_matvec(dm, x), O.matvec_bf16_ref(eye, x)[0])
+    rng = np.random.default_rng(33)
+    wi = S.bf16_from_f32(rng.integers(-20, 21, size=(300, 1000)).astype(np.float32))
+    xi = S.bf16_from_f32(rng.integers(-20, 21, size=1000).astype(np.float32))
+    dm = nwc.DeviceMatrix(nwc.encode(wi), DEV)
+    assert np.array_equal(run_matvec(dm, xi), O.matvec_bf16_ref(wi, xi)[0])
+
+
+# ----------------------------------------------------------------- fp8 variant of the single matrix
+def test_fp8_single_matrix():
+    w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
+    x = S.activation_bf16(C.SINGLE["x_seed"], 1024)
+    q, sc = S.fp8_quantize(w)
+    for cols in (0, 128, 256):
+        dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_item=cols), DEV)
+        assert np.array_equal(dequant_host(dm), O.decode_fp8(O.encode_fp8(q)))
+        y_ref, A = O.matvec_fp8_ref(q, sc, x)
+        check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8")
+
+
+def test_fp8_all_bytes_and_odd():
+    q = S.all_bytes_fp8(5)
+    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV)
+    assert np.array_equal(dequant_host(dm), q)
+    w = S.inject_rare(S.student_t_bf16(71, (1000, 3001)), 72)
+    q, sc = S.fp8_quantize(w)
+    x = S.activation_bf16(73, 3001)
+    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV)
+    assert np.array_equal(dequant_host(dm), q)
+    y_ref, A = O.matvec_fp8_ref(q, sc, x)
+    check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8 odd")
+
+
+# ----------------------------------------------------------------- full-size workloads
+def _device_matrix(seed, n, k, sigma):
+    wt = S.device_normal_bf16(seed, (n, k), sigma, DEV)
+    w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+    return wt, w
+
+
+def _sampled_matvec(dm, w, x, rows):
+    y = run_matvec(dm, x)
+    y_ref, A = O.matvec_bf16_ref(w[rows], x)
+    check_tol(y[rows], y_ref, A, f"sampled {w.shape}")
+    return y
+
+
+def _check_big(wt, w, seed, nsample=96):
+    n, k = w.shape
+    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
+    out = torch.empty((n, k), dtype=torch.int16, device=DEV)
+    dm.dequant(out)
+    assert torch.equal(out, wt.view(torch.int16)), "dequant differs from the input"
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, nsample)]))
+    enc_rows = O.encode_bf16(w[rows])          # oracle decode of the sampled rows
+    assert np.array_equal(O.decode_bf16(enc_rows), w[rows])
+    x = S.activation_bf16(seed + 1, k)
+    _sampled_matvec(dm, w, x, rows)
+    return dm
+
+
+def test_qwen3_4b_one_layer_full_size():
+    for idx, (name, n, k) in enumerate(C.QWEN3_4B):
+        ws, xs = C.qwen3_seed(0, idx)
+        print(f"qwen3 layer0 {name} {n}x{k}", flush=True)
+        wt, w = _device_matrix(ws, n, k, np.float32(C.sigma_for(k)))
+        _check_big(wt, w, xs)
+
+
+def test_tied_embedding_gather_and_lm_head():
+    n, k = C.EMBED_VOCAB, C.EMBED_HIDDEN
+    wt, w = _device_matrix(C.EMBED["w_seed"], n, k, 0.02)
+    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
+    ids = S.token_ids(C.EMBED["ids_seed"], n, C.N_IDS)
+    ids[:3] = [0, n - 1, ids[5]]
+    out = torch.empty((len(ids), k), dtype=torch.int16, device=DEV)
+    dm.gather(torch.from_numpy(ids).to(DEV), out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, wt.view(torch.int16)[torch.from_numpy(ids).to(DEV)])
+    x = S.activation_bf16(C.EMBED["x_seed"], k)
+    rows = np.unique(np.random.default_rng(3).integers(0, n, 256))
+    _sampled_matvec(dm, w, x, rows)
+
+
+def test_qwen25_7b_matrices_sampled():
+    for idx, (name, n, k) in enumerate(C.QWEN25_7B):
+        print(f"qwen2.5 layer0 {name} {n}x{k}", flush=True)
+        wt, w = _device_matrix(C.qwen25_seed(0, idx), n, k, np.float32(C.sigma_for(k)))
+        _check_big(wt, w, C.qwen25_seed(0, idx) + 7, nsample=32)

@@ -313,7 +313,8 @@ def test_fp8_matvec_exact_rationals():
 
 
 # --------------------------------------------------------------- whole workloads
-@pytest.mark.slow
+@pytest.mark.skipif(not os.environ.get("NWC_SLOW_ORACLE"),
+                    reason="36 x 7 full-size oracle round trips take hours on one core; set NWC_SLOW_ORACLE=1")
 def test_qwen3_layer_roundtrip_all():
     for layer in range(C.QWEN3_4B_LAYERS):
         for idx, (_, n, k) in enumerate(C.QWEN3_4B):

@@ -1,0 +1,239 @@
+"""Benchmark: fused compressed-BF16 GEMV over the Qwen3-4B layer set on one MI355X.
+
+One step = one sweep of the whole hot path over one batch of synthetic input:
+all 36 layers x 7 projections (q, k, v, o, gate, up, down) of a Qwen3-4B-shaped
+decoder, each a batch-1 nwc_matvec over its own compressed matrix, back to
+back on one stream.  The sweep reads ~4.9 GB of compressed weights, far more
+than the 256 MB last-level cache, so every matrix is read cold from HBM.
+
+Printed: one JSON line (the contract's fields plus roofline, cpu_baseline and
+per-shape figures).  Inputs are generated and encoded before the timed region;
+the timed region holds only kernel launches on resident data.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "fused compressed GEMV µs & compressed GB/s (% of HBM peak), Qwen3-4B layer set"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "nwc_format.h"):
+        h.update(open(os.path.join(ROOT, "decode_matvec_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(algo_bytes_per_launch: float):
+    """HBM bytes per launch measured by rocprofv3 PMC (committed), if they are of this kernel source."""
+    p = os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16):
+    mats = []
+    t0 = time.time()
+    for layer in range(layers):
+        for idx, (name, n, k) in enumerate(C.QWEN3_4B):
+            ws, xs = C.qwen3_seed(layer, idx)
+            wt = S.device_normal_bf16(ws, (n, k), np.float32(C.sigma_for(k)), dev)
+            w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+            blob = nwc.encode(w)
+            dm = nwc.DeviceMatrix(blob, dev)
+            x = S.activation_bf16(xs, k)
+            xd = torch.from_numpy(x.view(np.int16)).to(dev)
+            y = torch.empty(n, dtype=torch.float32, device=dev)
+            info = dm.info
+            mats.append(dict(name=name, n=n, k=k, dm=dm, x=xd, y=y, info=info,
+                             algo_bytes=info["coded_bits"] / 8.0 + 2 * k + 4 * n,
+                             blob_bytes=info["total_bytes"],
+                             w_bf16=wt if with_bf16 else None,
+                             x_bf16=xd.view(torch.bfloat16).view(1, k) if with_bf16 else None))
+            del w
+        if layer % 6 == 5 or layer == layers - 1:
+            log(f"[bench] encoded {layer + 1}/{layers} layers ({time.time() - t0:.1f}s)")
+    return mats
+
+
+def time_region(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call of fn
+
+
+def cpu_baseline(S, C):
+    """The oracle (decode + float64 matvec) on one q matrix of the layer set, on host cores."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    name, n, k = C.QWEN3_4B[1]  # k projection, 1024 x 2560
+    ws, xs = C.qwen3_seed(0, 1)
+    w = S.normal_bf16(ws, (n, k), C.sigma_for(k))  # host generator: same shape and distribution
+    x = S.activation_bf16(xs, k)
+    enc = O.encode_bf16(w)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    wd = O.decode_bf16(enc)
+    y, A = O.matvec_bf16_ref(wd, x)
+    dt = time.perf_counter() - t0
+    if ctx is not None:
+        ctx.unregister() if hasattr(ctx, "unregister") else None
+    gb = (enc["coded_bits"] / 8.0 + 2 * k + 4 * n) / 1e9
+    return {"value": round(gb / dt, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle decode + float64 matvec of one {n}x{k} matrix of the layer set "
+                      f"(host PCG64 draws of the same distribution), single thread, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth as S
+    from synth import configs as C
+    from decode_matvec_amd import nwc
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    mats = build_layer_set(torch, nwc, S, C, dev, args.layers, not args.no_bf16_baseline)
+    n_launch = len(mats)
+
+    def sweep():
+        for m in mats:
+            m["dm"].matvec(m["x"], m["y"])
+
+    # The sweep is captured once as a HIP graph and replayed: 252 launches per
+    # step from Python would otherwise be limited by host launch overhead,
+    # not by the GPU.  The eager (per-call ctypes launch) rate is reported too.
+    ms_eager = time_region(torch, sweep, max(2, args.steps // 4), 1)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sweep()  # warm the launch path on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        sweep()
+    torch.cuda.synchronize()
+    ms = time_region(torch, graph.replay, args.steps, args.warmup)
+    algo = sum(m["algo_bytes"] for m in mats)
+    blob = sum(m["blob_bytes"] for m in mats)
+    bf16_bytes = sum(2.0 * m["n"] * m["k"] for m in mats)
+    value = algo / (ms * 1e-3) / 1e9
+
+    per_shape = {}
+    for name, n, k in C.QWEN3_4B:
+        group = [m for m in mats if m["name"] == name]
+
+        def g_sweep(group=group):
+            for m in group:
+                m["dm"].matvec(m["x"], m["y"])
+
+        gg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gg):
+            g_sweep()
+        gms = time_region(torch, gg.replay, max(3, args.steps // 2), 1)
+        us = gms * 1e3 / len(group)
+        gb = sum(m["algo_bytes"] for m in group) / len(group)
+        per_shape[name] = {"shape": [n, k], "us": round(us, 3),
+                           "compressed_GBps": round(gb / (us * 1e-6) / 1e9, 1),
+                           "effective_bf16_GBps": round(2.0 * n * k / (us * 1e-6) / 1e9, 1),
+                           "blob_MB": round(group[0]["blob_bytes"] / 1e6, 3),
+                           "bits_per_weight_coded": round(group[0]["info"]["coded_bits"] / (n * k), 4),
+                           "bits_per_weight_blob": round(group[0]["blob_bytes"] * 8 / (n * k), 4),
+                           "cols_per_item": group[0]["info"]["cols_per_item"]}
+
+    bf16 = None
+    if not args.no_bf16_baseline:
+        F = torch.nn.functional
+
+        def bf16_sweep():
+            for m in mats:
+                F.linear(m["x_bf16"], m["w_bf16"])
+
+        bf16_sweep()  # library handles are created on first use, which capture forbids
+        torch.cuda.synchronize()
+        bg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bg):
+            bf16_sweep()
+        bms = time_region(torch, bg.replay, args.steps, args.warmup)
+        bf16 = {"ms_per_sweep": round(bms, 4),
+                "GBps": round((bf16_bytes + sum(2.0 * (m["n"] + m["k"]) for m in mats)) / (bms * 1e-3) / 1e9, 1),
+                "speedup_compressed_vs_bf16": round(bms / ms, 4),
+                "kernel": "torch.nn.functional.linear (hipBLASLt/rocBLAS), same rotation"}
+
+    algo_per_launch = algo / n_launch
+    achieved = algo_per_launch / (ms * 1e-3 / n_launch) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profiles(algo_per_launch)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on host cores")
+        cpu = cpu_baseline(S, C)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1/sqrt(K)) BF16 weights)",
+        "config": {"workload": "qwen3_4b_layer_set", "layers": args.layers, "matrices": n_launch,
+                   "batch": 1, "note": "36 x {q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, "
+                                       "down 2560x9728}, cold rotation"},
+        "us_per_layer": round(ms * 1e3 / args.layers, 2),
+        "timing": "HIP graph replay of the whole sweep on one stream; HIP events around the timed steps",
+        "ms_per_step_eager_launches": round(ms_eager, 4),
+        "us_per_matvec_avg": round(ms * 1e3 / n_launch, 3),
+        "hbm_frac_compressed": round(value / HBM_PEAK_GBPS, 4),
+        "effective_bf16_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1),
+        "blob_GBps": round(blob / (ms * 1e-3) / 1e9, 1),
+        "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(blob / 1e9, 4), "bf16_GB": round(bf16_bytes / 1e9, 4),
+        "per_shape": per_shape, "bf16_baseline": bf16, "roofline": roof, "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

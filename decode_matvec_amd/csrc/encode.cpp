@@ -402,7 +402,8 @@ int nwc_workspace_size(const void *header, int64_t *bytes) {
     *bytes = 0;
     return NWC_OK;
   }
-  *bytes = nwc_round_up((int64_t)h.n_items * NWC_LANES * 4, 256) + nwc_round_up((int64_t)h.n_rowblocks * 4, 256);
+  // fp32 partial sums [row][column span padded to a multiple of 4]
+  *bytes = nwc_round_up((int64_t)h.n_rowblocks * NWC_LANES * nwc_round_up(h.n_kspans, 4) * 4, 256);
   return NWC_OK;
 }
 

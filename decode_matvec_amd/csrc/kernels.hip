@@ -6,11 +6,13 @@
 // "Qwen3-4B-NWC-fp8" model card (scale applied after the row sum).  The
 // kernel design is this library's own, for CDNA4 wave64:
 //
-//  * One wave = one work item = 64 matrix rows x up to 256 columns.  Lane L
-//    owns row L, so the activation pair of a step is the same for every lane
-//    and lives in scalar registers; each lane keeps its own fp32 row sum and
-//    no cross-lane reduction is needed inside an item.
-//  * The item's code streams are staged once into LDS with coalesced 16-byte
+//  * A work item is 64 matrix rows x up to 256 columns; lane L owns row L, so
+//    the activation pair of a decode step is the same for every lane and no
+//    cross-lane reduction is needed inside an item.
+//  * A wave decodes NI items of consecutive row blocks at the same column span
+//    side by side (NI independent decode chains per lane), which hides LDS
+//    latency and shares the activation loads.
+//  * Each item's code streams are staged once into LDS with coalesced 16-byte
 //    loads, lane L's stream in LDS column L (bank L mod 32: conflict-free).
 //  * Each step a lane reads 64 bits of its stream at its own bit position
 //    (ds_read2st64), cuts a 12-bit peek with v_alignbit, and looks it up in a
@@ -21,29 +23,42 @@
 //    (escapes, long pairs) take a wave-uniform branch to an exact decoder.
 //  * Raw mantissa bytes stream from HBM with 16-byte per-lane loads laid out
 //    so a wave's load is one contiguous 1 KiB, prefetched four chunks ahead.
-//  * Column spans of one row block are summed by the last wave to finish
-//    (deterministic order, counters reset by that wave): one launch per matvec.
+//  * Column spans of one row block are summed by the last wave to finish, in
+//    a fixed order (counters reset by that wave): one launch per matvec.
 #include <hip/hip_runtime.h>
 
 #include "nwc_check.h"
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr uint32_t kSelLo = 0x05010400u;  // {m[0], hiA, m[1], hiB}
-constexpr uint32_t kSelHi = 0x05030402u;  // {m[2], hiA, m[3], hiB}
+constexpr uint32_t kSelLo = 0x05010400u;   // {m[0], hiA, m[1], hiB}
+constexpr uint32_t kSelHi = 0x05030402u;   // {m[2], hiA, m[3], hiB}
 constexpr uint32_t kSelPair = 0x05040100u; // {a.b0, a.b1, b.b0, b.b1}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 struct Geom {
   const uint8_t *blob;
   int64_t n, k;
-  uint32_t cols, n_kspans, n_items, last_cols, k_pad, region_words;
+  uint32_t cols, n_rowblocks, n_kspans, n_items, last_cols, k_pad, region_words;
   uint32_t r2s_lo, r2s_hi;  // rank_to_sym[0..7], one byte each
   uint64_t off_lut, off_items, off_mant, off_code;
 };
+
+// ----------------------------------------------------------------- LDS helpers
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(size_t)(const lds_u32 *)p;
+}
+__device__ __forceinline__ uint32_t lds_load(uint32_t byte_addr) { return *(const lds_u32 *)(size_t)byte_addr; }
+// Byte address of stream word (Q / 32) in the lane column starting at col_base.
+__device__ __forceinline__ uint32_t word_addr(uint32_t col_base, uint32_t Q) {
+  uint32_t a;
+  asm("v_lshl_add_u32 %0, %1, 8, %2" : "=v"(a) : "v"(Q >> 5), "v"(col_base));
+  return a;
+}
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, x), acc,
@@ -54,11 +69,10 @@ __device__ __forceinline__ uint32_t rank_sym(uint32_t r, uint32_t lo, uint32_t h
   return ((r < 4 ? lo : hi) >> ((r & 3) * 8)) & 0x7Fu;
 }
 
-// 64 stream bits of this lane starting at bit P (valid: at least 33).
-__device__ __forceinline__ uint64_t window64(const uint8_t *region, uint32_t lane4, uint32_t P) {
-  const uint32_t a = ((P >> 5) << 8) + lane4;
-  const uint32_t w0 = *(const uint32_t *)(region + a);
-  const uint32_t w1 = *(const uint32_t *)(region + a + 256);
+// 64 stream bits of a lane starting at bit P (at least 33 of them valid).
+__device__ __forceinline__ uint64_t window64(uint32_t col_base, uint32_t P) {
+  const uint32_t a = word_addr(col_base, P);
+  const uint32_t w0 = lds_load(a), w1 = lds_load(a + 256);
   return ((((uint64_t)w1) << 32) | w0) >> (P & 31);
 }
 
@@ -74,10 +88,9 @@ __device__ __forceinline__ void bf16_code(uint32_t v, uint32_t lo, uint32_t hi, 
   }
 }
 
-// Two BF16 codes at bit Q+2 in the table's entry format (slow path).
-__device__ __noinline__ uint32_t bf16_pair_exact(const uint8_t *region, uint32_t lane4, uint32_t Q, uint32_t lo,
-                                                 uint32_t hi) {
-  const uint64_t v = window64(region, lane4, Q + NWC_LEAD_BITS);
+// Two BF16 codes at bit Q+2, in the decode table's entry format (slow path).
+__device__ __noinline__ uint32_t bf16_pair_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
+  const uint64_t v = window64(col_base, Q + NWC_LEAD_BITS);
   uint32_t ha, la, hb, lb;
   bf16_code((uint32_t)v, lo, hi, ha, la);
   bf16_code((uint32_t)(v >> la), lo, hi, hb, lb);
@@ -95,10 +108,9 @@ __device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t b) {
   return (s << 15) | ((E + 120u) << 7) | (M << 4);
 }
 
-// One fp8 code at bit Q+2 in the table's entry format (slow path).
-__device__ __noinline__ uint32_t fp8_exact(const uint8_t *region, uint32_t lane4, uint32_t Q, uint32_t lo,
-                                           uint32_t hi) {
-  const uint32_t v = (uint32_t)window64(region, lane4, Q + NWC_LEAD_BITS);
+// One fp8 code at bit Q+2, in the decode table's entry format (slow path).
+__device__ __noinline__ uint32_t fp8_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
+  const uint32_t v = (uint32_t)window64(col_base, Q + NWC_LEAD_BITS);
   const uint32_t r = __builtin_ctz(~v | 0x100u);
   uint32_t s, E, M, len;
   if (r < NWC_ESCAPE_R) {
@@ -116,63 +128,68 @@ __device__ __noinline__ uint32_t fp8_exact(const uint8_t *region, uint32_t lane4
   return fp8_to_bf16(b) | (b << 16) | (len << 24);
 }
 
+// Decode state of one stream.
 struct Lane {
-  const uint8_t *region;  // this wave's staged code rows (LDS)
-  const uint8_t *lut;     // decode table (LDS)
-  uint32_t lane4;         // byte offset of this lane's column
-  uint32_t Q;             // stream bit position of the next code, minus 2
-  uint32_t lo, hi;        // rank_to_sym[0..7]
+  uint32_t col;  // LDS byte address of this lane's column (region + 4*lane)
+  uint32_t lut;  // LDS byte address of the decode table
+  uint32_t Q;    // stream bit position of the next code, minus 2
+  uint32_t lo, hi;
 };
 
-// Next two BF16 codes: returns {hiA, hiB, bits} entry.
-__device__ __forceinline__ uint32_t bf16_step(Lane &s) {
-  const uint32_t a = (__builtin_amdgcn_ubfe(s.Q, 5, 27) << 8) + s.lane4;  // row Q/32, column lane
-  const uint32_t w0 = *(const uint32_t *)(s.region + a);
-  const uint32_t w1 = *(const uint32_t *)(s.region + a + 256);
-  const uint32_t W = __builtin_amdgcn_alignbit(w1, w0, s.Q);  // bits Q..Q+31; peek = bits 2..13
-  uint32_t e = *(const uint32_t *)(s.lut + (W & 0x3FFCu));
-  if (__builtin_expect(__any((int)e < 0), 0)) e = bf16_pair_exact(s.region, s.lane4, s.Q, s.lo, s.hi);
-  s.Q += (e >> 16) & 0xFFu;
-  return e;
+// Next two BF16 codes of NI streams: e[i] = {hiA, hiB, bits} entries.
+template <int NI>
+__device__ __forceinline__ void bf16_steps(Lane (&s)[NI], uint32_t (&e)[NI]) {
+  uint32_t w0[NI], w1[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t a = word_addr(s[i].col, s[i].Q);
+    w0[i] = lds_load(a);
+    w1[i] = lds_load(a + 256);
+  }
+  uint32_t any = 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t W = __builtin_amdgcn_alignbit(w1[i], w0[i], s[i].Q);  // bits Q..Q+31; peek = bits 2..13
+    e[i] = lds_load(s[i].lut + (W & 0x3FFCu));
+    any |= e[i];
+  }
+  if (__builtin_expect(__any((int)any < 0), 0)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) e[i] = bf16_pair_exact(s[i].col, s[i].Q, s[i].lo, s[i].hi);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) s[i].Q += (e[i] >> 16) & 0xFFu;
 }
 
-// Next fp8 code: returns {bf16 value, byte, bits} entry.
+// Next fp8 code: returns {bf16 value, byte, bits}.
 __device__ __forceinline__ uint32_t fp8_step(Lane &s) {
-  const uint32_t a = (__builtin_amdgcn_ubfe(s.Q, 5, 27) << 8) + s.lane4;  // row Q/32, column lane
-  const uint32_t w0 = *(const uint32_t *)(s.region + a);
-  const uint32_t w1 = *(const uint32_t *)(s.region + a + 256);
-  const uint32_t W = __builtin_amdgcn_alignbit(w1, w0, s.Q);
-  uint32_t e = *(const uint32_t *)(s.lut + (W & 0x3FFCu));
-  if (__builtin_expect(__any((int)e < 0), 0)) e = fp8_exact(s.region, s.lane4, s.Q, s.lo, s.hi);
+  const uint32_t a = word_addr(s.col, s.Q);
+  const uint32_t W = __builtin_amdgcn_alignbit(lds_load(a + 256), lds_load(a), s.Q);
+  uint32_t e = lds_load(s.lut + (W & 0x3FFCu));
+  if (__builtin_expect(__any((int)e < 0), 0)) e = fp8_exact(s.col, s.Q, s.lo, s.hi);
   s.Q += e >> 24;
   return e;
 }
 
-struct Item {
-  uint32_t rb, ks, c0, ncols;
-  int64_t row;
-};
-
-__device__ __forceinline__ Item item_of(const Geom &g, uint32_t item, uint32_t lane) {
-  Item it;
-  it.rb = item / g.n_kspans;
-  it.ks = item - it.rb * g.n_kspans;
-  it.c0 = it.ks * g.cols;
-  it.ncols = it.ks == g.n_kspans - 1 ? g.last_cols : g.cols;
-  it.row = (int64_t)it.rb * 64 + lane;
-  return it;
+__device__ __forceinline__ uint32_t bf16_step(Lane &s) {
+  Lane one[1] = {s};
+  uint32_t e[1];
+  bf16_steps<1>(one, e);
+  s = one[0];
+  return e[0];
 }
 
-// Copies the 16 KiB table into LDS (whole workgroup).
-__device__ __forceinline__ void load_lut(const Geom &g, uint32_t *smem) {
+// Copies the 16 KiB decode table into LDS (whole workgroup).
+__device__ __forceinline__ void load_lut(const Geom &g, uint32_t *lut) {
   const uint4 *src = (const uint4 *)(g.blob + g.off_lut);
-  uint4 *dst = (uint4 *)smem;
+  uint4 *dst = (uint4 *)lut;
 #pragma unroll
-  for (int i = 0; i < NWC_LUT_BYTES / 16 / kThreads; ++i) dst[threadIdx.x + i * kThreads] = src[threadIdx.x + i * kThreads];
+  for (int i = 0; i < NWC_LUT_BYTES / 16 / kThreads; ++i)
+    dst[threadIdx.x + i * kThreads] = src[threadIdx.x + i * kThreads];
 }
 
-// Copies one item's code rows into the wave's LDS region (same layout).
-__device__ __forceinline__ void stage_item(const Geom &g, uint32_t item, uint32_t lane, uint8_t *region) {
+// Copies one item's code rows into an LDS region (same layout).
+__device__ __forceinline__ void stage_item(const Geom &g, uint32_t item, uint32_t lane, uint32_t *region) {
   const uint32_t *it = (const uint32_t *)(g.blob + g.off_items) + 2 * item;
   const uint32_t off = it[0], rows = it[1];
   const uint4 *src = (const uint4 *)(g.blob + g.off_code + off);
@@ -180,170 +197,273 @@ __device__ __forceinline__ void stage_item(const Geom &g, uint32_t item, uint32_
   for (uint32_t i = lane; i < rows * 16; i += 64) dst[i] = src[i];
 }
 
-__device__ __forceinline__ const uint4 *mant_base(const Geom &g, const Item &it, uint32_t lane) {
-  return (const uint4 *)(g.blob + g.off_mant + (uint64_t)it.rb * 64 * g.k_pad + (uint64_t)64 * it.c0) + lane;
+// Mantissa chunk 0 of this lane for item (rb, column c0); chunk j is at +64*j.
+__device__ __forceinline__ const uint4 *mant_base(const Geom &g, uint32_t rb, uint32_t c0, uint32_t lane) {
+  return (const uint4 *)(g.blob + g.off_mant + (uint64_t)rb * 64 * g.k_pad + (uint64_t)64 * c0) + lane;
 }
 
-// Activation pairs of 16 columns starting at item column `col` (zero past ncols).
-__device__ __forceinline__ void x_pairs(const uint16_t *x, const Item &it, uint32_t col, bool full, uint32_t xs[8]) {
-  if (full) {
-    const uint32_t *x32 = (const uint32_t *)(x + it.c0 + col);
+// A VGPR holding 0 that the compiler cannot see through.  Added to a uniform
+// address it keeps the load a vector load (vmcnt) rather than a scalar one,
+// whose completion every LDS wait would also have to wait for (lgkmcnt).
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// Activation pairs of 16 columns starting at absolute column c (all inside).
+struct X8 {
+  uint32_t v[8];
+};
+__device__ __forceinline__ X8 load_x8(const uint16_t *x, uint32_t c, uint32_t z) {
+  const uint4 *p = (const uint4 *)(x + c) + z;
+  const uint4 a = p[0], b = p[1];
+  return X8{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+}
+// Same for the last, partial group: columns c .. c+left-1, zero beyond.
+__device__ __forceinline__ X8 load_x8_tail(const uint16_t *x, uint32_t c, uint32_t left, uint32_t z) {
+  X8 r;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xs[j] = x32[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t c = col + 2 * j;
-      const uint32_t a = c < it.ncols ? x[it.c0 + c] : 0u;
-      const uint32_t b = c + 1 < it.ncols ? x[it.c0 + c + 1] : 0u;
-      xs[j] = a | (b << 16);
-    }
+  for (uint32_t j = 0; j < 8; ++j) {
+    const uint32_t a = 2 * j < left ? x[c + 2 * j + z] : 0u;
+    const uint32_t b = 2 * j + 1 < left ? x[c + 2 * j + 1 + z] : 0u;
+    r.v[j] = a | (b << 16);
   }
+  return r;
 }
 
 // ----------------------------------------------------------------- matvec
-__device__ __forceinline__ void mv_group_bf16(Lane &s, const uint4 &m, const uint32_t xs[8], float &a0, float &a1) {
-  const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t e = bf16_step(s);
-    const uint32_t p = __builtin_amdgcn_perm(e, mw[j >> 1], (j & 1) ? kSelHi : kSelLo);
-    if (j & 1)
-      a1 = dot2(p, xs[j], a1);
-    else
-      a0 = dot2(p, xs[j], a0);
-  }
-}
-
-__device__ __forceinline__ void mv_tail_bf16(Lane &s, const uint4 &m, const uint32_t xs[8], uint32_t left, float &a0,
-                                             float &a1) {
-  const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
+// One group (16 columns) of NI BF16 streams: 8 two-code steps each.
+template <int NI>
+__device__ __forceinline__ void mv_group_bf16(Lane (&s)[NI], const uint4 (&m)[NI], const X8 &x, float (&a0)[NI],
+                                              float (&a1)[NI], uint32_t left) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (2u * j >= left) break;
-    const uint32_t e = bf16_step(s);
-    uint32_t p = __builtin_amdgcn_perm(e, mw[j >> 1], (j & 1) ? kSelHi : kSelLo);
-    if (2u * j + 1 >= left) p &= 0xFFFFu;  // column past the matrix edge: not a weight
-    if (j & 1)
-      a1 = dot2(p, xs[j], a1);
-    else
-      a0 = dot2(p, xs[j], a0);
-  }
-}
-
-__device__ __forceinline__ void mv_group_fp8(Lane &s, const uint32_t xs[8], uint32_t left, float &a0, float &a1) {
+    uint32_t e[NI];
+    bf16_steps<NI>(s, e);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (2u * j >= left) break;
-    const uint32_t ea = fp8_step(s);
-    uint32_t eb = 0;
-    if (2u * j + 1 < left) eb = fp8_step(s);
-    const uint32_t p = __builtin_amdgcn_perm(eb, ea, kSelPair);
-    if (j & 1)
-      a1 = dot2(p, xs[j], a1);
-    else
-      a0 = dot2(p, xs[j], a0);
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t mw = (j >> 1) == 0 ? m[i].x : (j >> 1) == 1 ? m[i].y : (j >> 1) == 2 ? m[i].z : m[i].w;
+      uint32_t p = __builtin_amdgcn_perm(e[i], mw, (j & 1) ? kSelHi : kSelLo);
+      if (2u * j + 1 >= left) p &= 0xFFFFu;  // column past the matrix edge: not a weight
+      if (j & 1)
+        a1[i] = dot2(p, x.v[j], a1[i]);
+      else
+        a0[i] = dot2(p, x.v[j], a0[i]);
+    }
   }
 }
 
-// Row sum of one item for this lane.
-template <bool FP8>
-__device__ __forceinline__ float item_rowsum(const Geom &g, const Item &it, Lane &s, const uint16_t *x, uint32_t lane) {
+// Loads a matvec item needs before its first step, issued at kernel start so
+// that their HBM latency overlaps the staging of the code rows.
+template <int NI>
+struct MvPrefetch {
+  const uint4 *mp[NI];               // this lane's mantissa chunk 0 per item
+  uint4 m0[NI], m1[NI], m2[NI], m3[NI], mt[NI];  // chunks 0..3 (ring) and the partial chunk
+  X8 xc, xt;                         // activations of group 0 and of the partial group
+  uint32_t nfull, left, last, z;
+};
+
+// Every load is unconditional with its chunk/column index clamped to one that
+// exists (an item always has at least one 16-column chunk), so no merge of an
+// in-flight load makes the compiler wait for all of them.
+template <int NI>
+__device__ __forceinline__ void mv_prefetch(MvPrefetch<NI> &p, const Geom &g, const uint32_t (&rb)[NI], uint32_t c0,
+                                            uint32_t ncols, const uint16_t *x, uint32_t lane) {
+  p.nfull = ncols >> 4;
+  p.left = ncols & 15u;
+  p.last = p.nfull > 0 ? p.nfull - 1 : 0;
+  p.z = opaque_zero();
+  const uint32_t tail = p.left ? p.nfull : p.last;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    p.mp[i] = mant_base(g, rb[i], c0, lane);
+    p.m0[i] = p.mp[i][0];
+    p.m1[i] = p.mp[i][(1 < p.last ? 1 : p.last) * 64];
+    p.m2[i] = p.mp[i][(2 < p.last ? 2 : p.last) * 64];
+    p.m3[i] = p.mp[i][(3 < p.last ? 3 : p.last) * 64];
+    p.mt[i] = p.mp[i][tail * 64];
+  }
+  p.xt = load_x8_tail(x, c0 + tail * 16, p.left, p.z);
+  p.xc = p.xt;
+  if (p.nfull > 0) p.xc = load_x8(x, c0, p.z);
+}
+
+// Row sums of NI BF16 items (row blocks rb[i], same column span) for this lane.
+template <int NI>
+__device__ __forceinline__ void mv_run(MvPrefetch<NI> &p, Lane (&s)[NI], uint32_t c0, const uint16_t *x,
+                                       float (&out)[NI]) {
+  float a0[NI], a1[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) a0[i] = a1[i] = 0.f;
+  X8 xc = p.xc;
+  for (uint32_t g0 = 0; g0 < p.nfull; g0 += 4) {
+#pragma unroll
+    for (uint32_t r = 0; r < 4; ++r) {
+      const uint32_t gi = g0 + r;
+      if (gi >= p.nfull) break;
+      const uint32_t gn = gi + 1 < p.last ? gi + 1 : p.last;
+      const X8 xn = load_x8(x, c0 + gn * 16, p.z);
+      uint4 (&m)[NI] = r == 0 ? p.m0 : r == 1 ? p.m1 : r == 2 ? p.m2 : p.m3;
+      mv_group_bf16<NI>(s, m, xc, a0, a1, 16);
+      const uint32_t gf = gi + 4 < p.last ? gi + 4 : p.last;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) m[i] = p.mp[i][gf * 64];
+      xc = xn;
+    }
+  }
+  if (p.left) mv_group_bf16<NI>(s, p.mt, p.xt, a0, a1, p.left);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) out[i] = a0[i] + a1[i];
+}
+
+// Row sum of one fp8 item for this lane (one code per step).
+__device__ __forceinline__ float rowsum_fp8(uint32_t c0, uint32_t ncols, Lane &s, const uint16_t *x) {
+  const uint32_t z = opaque_zero();
   float a0 = 0.f, a1 = 0.f;
-  const uint32_t nfull = it.ncols >> 4, left = it.ncols & 15u;
-  uint32_t xs[8];
-  if (!FP8) {
-    const uint4 *mp = mant_base(g, it, lane);
-    const uint4 zero = {0u, 0u, 0u, 0u};
-    uint4 mt = left ? mp[nfull * 64] : zero;
-    uint4 m0 = nfull > 0 ? mp[0] : zero, m1 = nfull > 1 ? mp[64] : zero;
-    uint4 m2 = nfull > 2 ? mp[128] : zero, m3 = nfull > 3 ? mp[192] : zero;
-    for (uint32_t g0 = 0; g0 < nfull; g0 += 4) {
-      x_pairs(x, it, g0 * 16, true, xs);
-      mv_group_bf16(s, m0, xs, a0, a1);
-      if (g0 + 4 < nfull) m0 = mp[(g0 + 4) * 64];
-      if (g0 + 1 < nfull) {
-        x_pairs(x, it, (g0 + 1) * 16, true, xs);
-        mv_group_bf16(s, m1, xs, a0, a1);
-        if (g0 + 5 < nfull) m1 = mp[(g0 + 5) * 64];
-      }
-      if (g0 + 2 < nfull) {
-        x_pairs(x, it, (g0 + 2) * 16, true, xs);
-        mv_group_bf16(s, m2, xs, a0, a1);
-        if (g0 + 6 < nfull) m2 = mp[(g0 + 6) * 64];
-      }
-      if (g0 + 3 < nfull) {
-        x_pairs(x, it, (g0 + 3) * 16, true, xs);
-        mv_group_bf16(s, m3, xs, a0, a1);
-        if (g0 + 7 < nfull) m3 = mp[(g0 + 7) * 64];
-      }
-    }
-    if (left) {
-      x_pairs(x, it, nfull * 16, false, xs);
-      mv_tail_bf16(s, mt, xs, left, a0, a1);
-    }
-  } else {
-    for (uint32_t gi = 0; gi < nfull; ++gi) {
-      x_pairs(x, it, gi * 16, true, xs);
-      mv_group_fp8(s, xs, 16, a0, a1);
-    }
-    if (left) {
-      x_pairs(x, it, nfull * 16, false, xs);
-      mv_group_fp8(s, xs, left, a0, a1);
+  for (uint32_t col = 0; col < ncols; col += 16) {
+    const uint32_t left = ncols - col < 16 ? ncols - col : 16;
+    const X8 xv = left == 16 ? load_x8(x, c0 + col, z) : load_x8_tail(x, c0 + col, left, z);
+#pragma unroll
+    for (uint32_t j = 0; j < 8; ++j) {
+      if (2 * j >= left) break;
+      const uint32_t ea = fp8_step(s);
+      const uint32_t eb = 2 * j + 1 < left ? fp8_step(s) : 0u;
+      const uint32_t p = __builtin_amdgcn_perm(eb, ea, kSelPair);
+      if (j & 1)
+        a1 = dot2(p, xv.v[j], a1);
+      else
+        a0 = dot2(p, xv.v[j], a0);
     }
   }
   return a0 + a1;
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(kThreads) void matvec_kernel(Geom g, const uint16_t *__restrict__ x,
+// ----------------------------------------------------------------- async staging
+typedef __attribute__((address_space(3))) void lds_void;
+
+// This wave's share of a copy global -> LDS: 1 KiB per instruction straight
+// into LDS (no registers), lane L moving bytes [16L, 16L+16) of each KiB.
+__device__ __forceinline__ void dma_to_lds(const uint8_t *src, uint32_t *dst, uint32_t bytes, uint32_t lane) {
+  for (uint32_t off = 0; off < bytes; off += 1024)
+    if (off + lane * 16 < bytes)
+      __builtin_amdgcn_global_load_lds(src + off + lane * 16, (lds_void *)((uint8_t *)dst + off), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Partial sums live at [row][column span], each row padded to a multiple of
+// 4 spans (16-byte loads in the reduction).
+__device__ __forceinline__ uint32_t kspans_pad(uint32_t n_kspans) { return (n_kspans + 3u) & ~3u; }
+
+// Wave w of the grid decodes row blocks NI*j .. NI*j+NI-1 at column span ks,
+// where w = j * n_kspans + ks, and writes y (one span) or its partial sums.
+template <bool FP8, int NI>
+__global__ __launch_bounds__(kThreads) void matvec_kernel(Geom g, const uint32_t *__restrict__ items,
+                                                          const uint16_t *__restrict__ x,
                                                           const float *__restrict__ scale, float *__restrict__ y,
-                                                          float *__restrict__ partial, uint32_t *__restrict__ count) {
+                                                          float *__restrict__ partial) {
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
   extern __shared__ uint32_t s_code[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t item = blockIdx.x * kWaves + wave;
-  uint8_t *region = (uint8_t *)(s_code + wave * g.region_words);
-  load_lut(g, s_lut);
-  const bool active = item < g.n_items;
-  if (active) stage_item(g, item, lane, region);
+  const uint32_t witem = blockIdx.x * kWaves + wave;
+  const uint32_t n_groups = (g.n_rowblocks + NI - 1) / NI;
+  const bool active = witem < n_groups * g.n_kspans;
+  const uint32_t grp = active ? witem / g.n_kspans : 0, ks = active ? witem - grp * g.n_kspans : 0;
+  const uint32_t c0 = ks * g.cols;
+  const uint32_t ncols = ks == g.n_kspans - 1 ? g.last_cols : g.cols;
+
+  // Issue everything the first step needs, then wait once.  The item table
+  // entries are wave-uniform scalar loads, so waiting for them (lgkmcnt) does
+  // not wait for the decode-table copy already in flight (vmcnt).
+  uint32_t rb[NI], code_off[NI], code_rows[NI];
+  uint32_t *region[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t r = grp * NI + i;
+    rb[i] = r < g.n_rowblocks ? r : g.n_rowblocks - 1;
+    region[i] = s_code + (wave * NI + i) * g.region_words;
+    code_off[i] = items[2 * (rb[i] * g.n_kspans + ks)];
+    code_rows[i] = items[2 * (rb[i] * g.n_kspans + ks) + 1];
+  }
+  dma_to_lds(g.blob + g.off_lut + wave * (NWC_LUT_BYTES / kWaves), s_lut + wave * (NWC_LUT_ENTRIES / kWaves),
+             NWC_LUT_BYTES / kWaves, lane);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (active) dma_to_lds(g.blob + g.off_code + code_off[i], region[i], code_rows[i] * 256, lane);
+  MvPrefetch<NI> pf;
+  if (!FP8 && active) mv_prefetch<NI>(pf, g, rb, c0, ncols, x, lane);
+  wait_all_loads();
   __syncthreads();
   if (!active) return;
 
-  const Item it = item_of(g, item, lane);
-  Lane s{region, (const uint8_t *)s_lut, lane * 4u, 0u, g.r2s_lo, g.r2s_hi};
-  float acc = item_rowsum<FP8>(g, it, s, x, lane);
-
-  if (g.n_kspans == 1) {
-    if (it.row < g.n) y[it.row] = FP8 ? acc * scale[it.row] : acc;
-    return;
+  const uint32_t lut = lds_addr(s_lut);
+  float acc[NI];
+  if (FP8) {
+    Lane s{lds_addr(region[0]) + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
+    acc[0] = rowsum_fp8(c0, ncols, s, x);
+  } else {
+    Lane s[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) s[i] = Lane{lds_addr(region[i]) + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
+    mv_run<NI>(pf, s, c0, x, acc);
   }
-  __hip_atomic_store(partial + (uint64_t)item * 64 + lane, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __threadfence();
-  uint32_t done = 0;
-  if (lane == 0) done = atomicAdd(count + it.rb, 1u);
-  done = __builtin_amdgcn_readfirstlane(done);
-  if (done != g.n_kspans - 1) return;
-  __threadfence();
+  const uint32_t kp = kspans_pad(g.n_kspans);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (grp * NI + i >= g.n_rowblocks) continue;
+    const int64_t row = (int64_t)rb[i] * 64 + lane;
+    if (g.n_kspans == 1) {
+      if (row < g.n) y[row] = FP8 ? acc[i] * scale[row] : acc[i];
+    } else {
+      partial[(uint64_t)row * kp + ks] = acc[i];
+    }
+  }
+}
+
+// y[row] = (scale[row] *) sum over column spans of the partials, 16 threads
+// per row: thread j sums 16-byte chunks j, j+16, ... in order, then a fixed
+// butterfly over the 16 threads.  Same order every call.
+template <bool FP8>
+__global__ __launch_bounds__(256) void reduce_kernel(const float *__restrict__ partial, uint32_t n_kspans, int64_t n,
+                                                     const float *__restrict__ scale, float *__restrict__ y) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = t >> 4;
+  const uint32_t j = (uint32_t)t & 15u;
+  const uint32_t kp = kspans_pad(n_kspans);
   float sum = 0.f;
-  const float *p = partial + (uint64_t)it.rb * g.n_kspans * 64 + lane;
-  for (uint32_t j = 0; j < g.n_kspans; ++j)
-    sum += __hip_atomic_load(p + (uint64_t)j * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (it.row < g.n) y[it.row] = FP8 ? sum * scale[it.row] : sum;
-  if (lane == 0) __hip_atomic_store(count + it.rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (row < n) {
+    const float4 *p = (const float4 *)(partial + (uint64_t)row * kp);
+    for (uint32_t c = j; c < kp / 4; c += 16) {
+      const float4 v = p[c];
+      sum += v.x;
+      if (4 * c + 1 < n_kspans) sum += v.y;
+      if (4 * c + 2 < n_kspans) sum += v.z;
+      if (4 * c + 3 < n_kspans) sum += v.w;
+    }
+  }
+  sum += __shfl_xor(sum, 8, 16);
+  sum += __shfl_xor(sum, 4, 16);
+  sum += __shfl_xor(sum, 2, 16);
+  sum += __shfl_xor(sum, 1, 16);
+  if (j == 0 && row < n) y[row] = FP8 ? sum * scale[row] : sum;
 }
 
 // ----------------------------------------------------------------- dequant / gather
 // Decodes the lane's item stream and hands each BF16 pair (or fp8 byte) to out.
 template <bool FP8, class Out>
-__device__ __forceinline__ void item_decode(const Geom &g, const Item &it, Lane &s, const uint4 *mp, Out &out) {
-  const uint32_t nsteps = FP8 ? it.ncols : (it.ncols + 1) / 2;
-  for (uint32_t gi = 0; gi * 16 < it.ncols; ++gi) {
+__device__ __forceinline__ void item_decode(uint32_t ncols, Lane &s, const uint4 *mp, Out &out) {
+  const uint32_t nsteps = FP8 ? ncols : (ncols + 1) / 2;
+  for (uint32_t gi = 0; gi * 16 < ncols; ++gi) {
     uint32_t mw[4] = {0u, 0u, 0u, 0u};
     if (!FP8) {
       const uint4 m = mp[gi * 64];
-      mw[0] = m.x; mw[1] = m.y; mw[2] = m.z; mw[3] = m.w;
+      mw[0] = m.x;
+      mw[1] = m.y;
+      mw[2] = m.z;
+      mw[3] = m.w;
     }
     const uint32_t per = FP8 ? 16u : 8u;
 #pragma unroll
@@ -361,9 +481,9 @@ __device__ __forceinline__ void item_decode(const Geom &g, const Item &it, Lane 
   }
 }
 
-// Writes one row segment; pairs for columns past ncols are dropped.
+// Writes one row segment; elements of columns past ncols are dropped.
 struct RowOut {
-  uint8_t *dst;    // element (row, c0)
+  uint8_t *dst;  // element (row, c0)
   uint32_t ncols;
   bool ok;
   __device__ __forceinline__ void put16(uint32_t c, uint32_t pair) {
@@ -384,19 +504,22 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(Geom g, uint8_t *__re
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t item = blockIdx.x * kWaves + wave;
-  uint8_t *region = (uint8_t *)(s_code + wave * g.region_words);
+  uint32_t *region = s_code + wave * g.region_words;
   load_lut(g, s_lut);
   const bool active = item < g.n_items;
   if (active) stage_item(g, item, lane, region);
   __syncthreads();
   if (!active) return;
-  const Item it = item_of(g, item, lane);
-  Lane s{region, (const uint8_t *)s_lut, lane * 4u, 0u, g.r2s_lo, g.r2s_hi};
+  const uint32_t rb = item / g.n_kspans, ks = item - rb * g.n_kspans;
+  const uint32_t c0 = ks * g.cols, ncols = ks == g.n_kspans - 1 ? g.last_cols : g.cols;
+  const int64_t row = (int64_t)rb * 64 + lane;
+  Lane s{lds_addr(region) + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
   const int64_t esz = FP8 ? 1 : 2;
-  RowOut out{w + (it.row * ld + it.c0) * esz, it.ncols, it.row < g.n};
-  item_decode<FP8>(g, it, s, FP8 ? nullptr : mant_base(g, it, lane), out);
+  RowOut out{w + (row * ld + c0) * esz, ncols, row < g.n};
+  item_decode<FP8>(ncols, s, FP8 ? nullptr : mant_base(g, rb, c0, lane), out);
 }
 
+// Thread t decodes row ids[t] (its lane's own stream column in LDS).
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void gather_kernel(Geom g, const int64_t *__restrict__ ids, int64_t n_ids,
                                                           uint8_t *__restrict__ out) {
@@ -404,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(Geom g, const int64_t 
   extern __shared__ uint32_t s_code[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint8_t *region = (uint8_t *)(s_code + wave * g.region_words);
+  uint32_t *region = s_code + wave * g.region_words;
   load_lut(g, s_lut);
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -419,21 +542,15 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(Geom g, const int64_t 
     const uint32_t *ie = (const uint32_t *)(g.blob + g.off_items) + 2 * item;
     const uint32_t off = ie[0], rows = ie[1];
     const uint32_t *src = (const uint32_t *)(g.blob + g.off_code + off) + L;
-    uint32_t *dst = (uint32_t *)region + lane;
+    uint32_t *dst = region + lane;
     for (uint32_t r = 0; r < rows; ++r) dst[r * 64] = src[r * 64];
-    Item it;
-    it.rb = rb;
-    it.ks = ks;
-    it.c0 = ks * g.cols;
-    it.ncols = ks == g.n_kspans - 1 ? g.last_cols : g.cols;
-    it.row = row;
-    Lane s{region, (const uint8_t *)s_lut, lane * 4u, 0u, g.r2s_lo, g.r2s_hi};
-    RowOut o{out + (t * g.k + it.c0) * esz, it.ncols, live};
-    const uint4 *mp = FP8 ? nullptr : mant_base(g, it, L);
+    const uint32_t c0 = ks * g.cols, ncols = ks == g.n_kspans - 1 ? g.last_cols : g.cols;
+    Lane s{lds_addr(region) + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
+    RowOut o{out + (t * g.k + c0) * esz, ncols, live};
     if (valid) {
-      item_decode<FP8>(g, it, s, mp, o);
+      item_decode<FP8>(ncols, s, FP8 ? nullptr : mant_base(g, rb, c0, L), o);
     } else if (live) {
-      for (uint32_t c = 0; c < it.ncols * esz; ++c) o.dst[c] = 0;
+      for (uint32_t c = 0; c < ncols * esz; ++c) o.dst[c] = 0;
     }
   }
 }
@@ -444,6 +561,7 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
   g.n = h.n;
   g.k = h.k;
   g.cols = h.cols_per_item;
+  g.n_rowblocks = h.n_rowblocks;
   g.n_kspans = h.n_kspans;
   g.n_items = h.n_items;
   g.last_cols = h.last_cols;
@@ -458,8 +576,21 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
   return g;
 }
 
-// Dynamic LDS: the waves' code regions (the decode table is static LDS).
-size_t lds_bytes(const Geom &g) { return (size_t)kWaves * g.region_words * 4; }
+// Dynamic LDS: per wave, `chains` staged code regions (the table is static LDS).
+size_t lds_bytes(const Geom &g, int chains) { return (size_t)kWaves * chains * g.region_words * 4; }
+
+constexpr size_t kMaxDynamicLds = 48 * 1024;  // + 16 KiB static table = 64 KiB per workgroup
+
+// Decode chains per wave for a BF16 matvec.  One: every wave of a typical
+// matrix is resident at once, so a wave's lifetime sets the kernel time and a
+// second chain only lengthens it.  NWC_CHAINS=2|4 selects more for experiments.
+int matvec_chains(const Geom &g) {
+  if (const char *e = getenv("NWC_CHAINS")) {
+    const int v = atoi(e);
+    if ((v == 1 || v == 2 || v == 4) && lds_bytes(g, v) <= kMaxDynamicLds) return v;
+  }
+  return 1;
+}
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -469,6 +600,17 @@ int read_header(const void *header, nwc_header_t &h) {
   if (!header) return NWC_ERR_ARG;
   memcpy(&h, header, sizeof h);
   return nwc_check_header(&h);
+}
+
+template <bool FP8, int NI>
+void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
+  const uint32_t waves = (g.n_rowblocks + NI - 1) / NI * g.n_kspans;
+  const dim3 grid((waves + kWaves - 1) / kWaves), block(kThreads);
+  hipLaunchKernelGGL((matvec_kernel<FP8, NI>), grid, block, lds_bytes(g, NI), s, g,
+                     (const uint32_t *)(g.blob + g.off_items), (const uint16_t *)d_x, d_scale, d_y, partial);
+  if (g.n_kspans > 1)
+    hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
+                       g.n_kspans, g.n, d_scale, d_y);
 }
 
 }  // namespace
@@ -486,22 +628,22 @@ int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const fl
   int64_t need = 0;
   if ((st = nwc_workspace_size(header, &need)) != NWC_OK) return st;
   float *partial = nullptr;
-  uint32_t *count = nullptr;
   if (need > 0) {
     if (!d_ws || !aligned(d_ws, 256)) return NWC_ERR_ARG;
     if (ws_bytes < need) return NWC_ERR_CAPACITY;
     partial = (float *)d_ws;
-    count = (uint32_t *)((uint8_t *)d_ws + nwc_round_up((int64_t)h.n_items * 64 * 4, 256));
   }
   const Geom g = make_geom(h, d_blob);
-  const dim3 grid((h.n_items + kWaves - 1) / kWaves), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
-  if (fp8)
-    hipLaunchKernelGGL(matvec_kernel<true>, grid, block, lds_bytes(g), s, g, (const uint16_t *)d_x, d_scale, d_y,
-                       partial, count);
-  else
-    hipLaunchKernelGGL(matvec_kernel<false>, grid, block, lds_bytes(g), s, g, (const uint16_t *)d_x, d_scale, d_y,
-                       partial, count);
+  if (fp8) {
+    launch_matvec<true, 1>(g, s, d_x, d_scale, d_y, partial);
+  } else {
+    switch (matvec_chains(g)) {
+      case 4: launch_matvec<false, 4>(g, s, d_x, d_scale, d_y, partial); break;
+      case 2: launch_matvec<false, 2>(g, s, d_x, d_scale, d_y, partial); break;
+      default: launch_matvec<false, 1>(g, s, d_x, d_scale, d_y, partial); break;
+    }
+  }
   return launched();
 }
 
@@ -515,9 +657,9 @@ int nwc_dequant(const void *header, const void *d_blob, void *d_w, int64_t ld, v
   const dim3 grid((h.n_items + kWaves - 1) / kWaves), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   if (h.elem == NWC_FP8_E4M3)
-    hipLaunchKernelGGL(dequant_kernel<true>, grid, block, lds_bytes(g), s, g, (uint8_t *)d_w, ld);
+    hipLaunchKernelGGL(dequant_kernel<true>, grid, block, lds_bytes(g, 1), s, g, (uint8_t *)d_w, ld);
   else
-    hipLaunchKernelGGL(dequant_kernel<false>, grid, block, lds_bytes(g), s, g, (uint8_t *)d_w, ld);
+    hipLaunchKernelGGL(dequant_kernel<false>, grid, block, lds_bytes(g, 1), s, g, (uint8_t *)d_w, ld);
   return launched();
 }
 
@@ -534,9 +676,9 @@ int nwc_gather(const void *header, const void *d_blob, const int64_t *d_ids, int
   const dim3 grid((unsigned)((n_ids + kThreads - 1) / kThreads)), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   if (h.elem == NWC_FP8_E4M3)
-    hipLaunchKernelGGL(gather_kernel<true>, grid, block, lds_bytes(g), s, g, d_ids, n_ids, (uint8_t *)d_out);
+    hipLaunchKernelGGL(gather_kernel<true>, grid, block, lds_bytes(g, 1), s, g, d_ids, n_ids, (uint8_t *)d_out);
   else
-    hipLaunchKernelGGL(gather_kernel<false>, grid, block, lds_bytes(g), s, g, d_ids, n_ids, (uint8_t *)d_out);
+    hipLaunchKernelGGL(gather_kernel<false>, grid, block, lds_bytes(g, 1), s, g, d_ids, n_ids, (uint8_t *)d_out);
   return launched();
 }
 

@@ -158,7 +158,7 @@ class DeviceMatrix:
         self.header = np.ascontiguousarray(blob[:HEADER_BYTES]).copy()
         self.d_blob = torch.from_numpy(blob).to(device)
         wsb = workspace_size(self.header)
-        self.ws = torch.zeros(max(wsb, 0) // 4, dtype=torch.int32, device=device) if wsb else None
+        self.ws = torch.empty(wsb // 4, dtype=torch.int32, device=device) if wsb else None
         self.n, self.k = self.info["n"], self.info["k"]
         self.elem = self.info["elem"]
         self.nbytes = int(blob.nbytes)

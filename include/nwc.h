@@ -97,9 +97,8 @@ int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, i
 int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info);
 
 /* Device workspace bytes nwc_matvec needs for this blob (0 if the matrix has
- * a single column span).  Layout: fp32 partial sums, then one 32-bit counter
- * per 64-row block.  The counters must be zero before the first call (for
- * example a zero-filled allocation); every call leaves them zero again. */
+ * a single column span): fp32 partial sums of each row per column span.  Its
+ * contents need no initialisation and are overwritten by every call. */
 int nwc_workspace_size(const void *header, int64_t *bytes);
 
 /* Fused decode + matvec ("Fused kernel": weights decoded in registers, fp32
@@ -110,7 +109,9 @@ int nwc_workspace_size(const void *header, int64_t *bytes);
  *   d_ws     device workspace of ws_bytes >= nwc_workspace_size, 256-byte
  *            aligned; may be NULL when the size is 0.  Concurrent calls need
  *            distinct workspaces.
- * The summation order is fixed, so repeated calls give identical bits. */
+ * Enqueues the fused kernel and, for matrices with more than one column span,
+ * a second small kernel that sums the spans' partials.  The summation order
+ * is fixed, so repeated calls give identical bits. */
 int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const float *d_scale,
                float *d_y, void *d_ws, int64_t ws_bytes, void *stream);
 

@@ -153,7 +153,8 @@ def test_header_validation_and_workspace():
     ws = nwc.workspace_size(hdr)
     info = nwc.blob_info(blob)
     n_rb = (200 + 63) // 64
-    assert ws == ((info["n_items"] * 64 * 4 + 255) // 256) * 256 + 256
+    n_ks_pad = (((700 + 127) // 128) + 3) // 4 * 4
+    assert ws == ((n_rb * 64 * n_ks_pad * 4 + 255) // 256) * 256
     assert info["n_items"] == n_rb * ((700 + 127) // 128)
     bad = hdr.copy()
     bad[0] ^= 1

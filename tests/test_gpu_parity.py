@@ -181,8 +181,8 @@ def _check_big(wt, w, seed, nsample=96):
     assert torch.equal(out, wt.view(torch.int16)), "dequant differs from the input"
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, nsample)]))
-    enc_rows = O.encode_bf16(w[rows])          # oracle decode of the sampled rows
-    assert np.array_equal(O.decode_bf16(enc_rows), w[rows])
+    enc_rows = O.encode_bf16(w[rows[:6]])      # oracle decode of a few sampled rows
+    assert np.array_equal(O.decode_bf16(enc_rows), w[rows[:6]])
     x = S.activation_bf16(seed + 1, k)
     _sampled_matvec(dm, w, x, rows)
     return dm

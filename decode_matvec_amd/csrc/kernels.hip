@@ -23,8 +23,9 @@
 //    (escapes, long pairs) take a wave-uniform branch to an exact decoder.
 //  * Raw mantissa bytes stream from HBM with 16-byte per-lane loads laid out
 //    so a wave's load is one contiguous 1 KiB, prefetched four chunks ahead.
-//  * Column spans of one row block are summed by the last wave to finish, in
-//    a fixed order (counters reset by that wave): one launch per matvec.
+//  * Each wave stores its item's 64 row sums as plain fp32 partials; when a
+//    matrix has more than one column span, a second small kernel sums each
+//    row's partials in a fixed order (deterministic, no atomics, no fences).
 #include <hip/hip_runtime.h>
 
 #include "nwc_check.h"
@@ -255,65 +256,72 @@ __device__ __forceinline__ void mv_group_bf16(Lane (&s)[NI], const uint4 (&m)[NI
   }
 }
 
-// Loads a matvec item needs before its first step, issued at kernel start so
-// that their HBM latency overlaps the staging of the code rows.
-template <int NI>
+// Loads a matvec item needs before its first step.  The mantissa chunks go
+// through a ring of depth D: chunks 0..D-1 are requested in the prologue and
+// chunk g+D while group g decodes, so an item's bytes are requested as its
+// decode progresses rather than all at kernel start (with every wave of a
+// matrix resident at once, the latter queues the whole matrix in HBM ahead of
+// the first decode step).
+template <int NI, int D>
 struct MvPrefetch {
-  const uint4 *mp[NI];               // this lane's mantissa chunk 0 per item
-  uint4 m0[NI], m1[NI], m2[NI], m3[NI], mt[NI];  // chunks 0..3 (ring) and the partial chunk
-  X8 xc, xt;                         // activations of group 0 and of the partial group
+  const uint4 *mp[NI];  // this lane's mantissa chunk 0 per item
+  uint4 m[D][NI];       // the ring
+  X8 xc;                // activations of group 0
   uint32_t nfull, left, last, z;
 };
 
-// Every load is unconditional with its chunk/column index clamped to one that
-// exists (an item always has at least one 16-column chunk), so no merge of an
-// in-flight load makes the compiler wait for all of them.
-template <int NI>
-__device__ __forceinline__ void mv_prefetch(MvPrefetch<NI> &p, const Geom &g, const uint32_t (&rb)[NI], uint32_t c0,
-                                            uint32_t ncols, const uint16_t *x, uint32_t lane) {
+// Issued after the item's direct-to-LDS copies: the activations of group 0
+// (skipped for an item without a full group), then exactly D*NI mantissa
+// chunk loads.  The kernel then waits with vmcnt(D*NI) -- for the copies and
+// the activations only.  Chunk indices are clamped to one that exists (an
+// item always has at least one 16-column chunk), so every load is
+// unconditional and no merge of an in-flight load makes the compiler wait for
+// all of them.
+template <int NI, int D>
+__device__ __forceinline__ void mv_prefetch(MvPrefetch<NI, D> &p, const Geom &g, const uint32_t (&rb)[NI],
+                                            uint32_t c0, uint32_t ncols, const uint16_t *x, uint32_t lane) {
   p.nfull = ncols >> 4;
   p.left = ncols & 15u;
   p.last = p.nfull > 0 ? p.nfull - 1 : 0;
   p.z = opaque_zero();
-  const uint32_t tail = p.left ? p.nfull : p.last;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    p.mp[i] = mant_base(g, rb[i], c0, lane);
-    p.m0[i] = p.mp[i][0];
-    p.m1[i] = p.mp[i][(1 < p.last ? 1 : p.last) * 64];
-    p.m2[i] = p.mp[i][(2 < p.last ? 2 : p.last) * 64];
-    p.m3[i] = p.mp[i][(3 < p.last ? 3 : p.last) * 64];
-    p.mt[i] = p.mp[i][tail * 64];
-  }
-  p.xt = load_x8_tail(x, c0 + tail * 16, p.left, p.z);
-  p.xc = p.xt;
   if (p.nfull > 0) p.xc = load_x8(x, c0, p.z);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) p.mp[i] = mant_base(g, rb[i], c0, lane);
+#pragma unroll
+  for (int r = 0; r < D; ++r)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) p.m[r][i] = p.mp[i][((uint32_t)r < p.last ? (uint32_t)r : p.last) * 64];
 }
 
 // Row sums of NI BF16 items (row blocks rb[i], same column span) for this lane.
-template <int NI>
-__device__ __forceinline__ void mv_run(MvPrefetch<NI> &p, Lane (&s)[NI], uint32_t c0, const uint16_t *x,
+template <int NI, int D>
+__device__ __forceinline__ void mv_run(MvPrefetch<NI, D> &p, Lane (&s)[NI], uint32_t c0, const uint16_t *x,
                                        float (&out)[NI]) {
   float a0[NI], a1[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) a0[i] = a1[i] = 0.f;
   X8 xc = p.xc;
-  for (uint32_t g0 = 0; g0 < p.nfull; g0 += 4) {
+  for (uint32_t g0 = 0; g0 < p.nfull; g0 += D) {
 #pragma unroll
-    for (uint32_t r = 0; r < 4; ++r) {
+    for (uint32_t r = 0; r < (uint32_t)D; ++r) {
       const uint32_t gi = g0 + r;
       if (gi >= p.nfull) break;
       const uint32_t gn = gi + 1 < p.last ? gi + 1 : p.last;
       const X8 xn = load_x8(x, c0 + gn * 16, p.z);
-      uint4 (&m)[NI] = r == 0 ? p.m0 : r == 1 ? p.m1 : r == 2 ? p.m2 : p.m3;
-      mv_group_bf16<NI>(s, m, xc, a0, a1, 16);
-      const uint32_t gf = gi + 4 < p.last ? gi + 4 : p.last;
+      mv_group_bf16<NI>(s, p.m[r], xc, a0, a1, 16);
+      const uint32_t gf = gi + D < p.last ? gi + D : p.last;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) m[i] = p.mp[i][gf * 64];
+      for (int i = 0; i < NI; ++i) p.m[r][i] = p.mp[i][gf * 64];
       xc = xn;
     }
   }
-  if (p.left) mv_group_bf16<NI>(s, p.mt, p.xt, a0, a1, p.left);
+  if (p.left) {
+    uint4 mt[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) mt[i] = p.mp[i][p.nfull * 64];
+    const X8 xt = load_x8_tail(x, c0 + p.nfull * 16, p.left, p.z);
+    mv_group_bf16<NI>(s, mt, xt, a0, a1, p.left);
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) out[i] = a0[i] + a1[i];
 }
@@ -352,6 +360,15 @@ __device__ __forceinline__ void dma_to_lds(const uint8_t *src, uint32_t *dst, ui
 }
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N vector loads are outstanding: with N mantissa loads
+// issued last, this waits for everything issued before them.
+template <int N>
+__device__ __forceinline__ void wait_copies_before(bool issued) {
+  if (issued)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  else
+    wait_all_loads();
+}
 
 // Partial sums live at [row][column span], each row padded to a multiple of
 // 4 spans (16-byte loads in the reduction).
@@ -359,7 +376,7 @@ __device__ __forceinline__ uint32_t kspans_pad(uint32_t n_kspans) { return (n_ks
 
 // Wave w of the grid decodes row blocks NI*j .. NI*j+NI-1 at column span ks,
 // where w = j * n_kspans + ks, and writes y (one span) or its partial sums.
-template <bool FP8, int NI>
+template <bool FP8, int NI, int D>
 __global__ __launch_bounds__(kThreads) void matvec_kernel(Geom g, const uint32_t *__restrict__ items,
                                                           const uint16_t *__restrict__ x,
                                                           const float *__restrict__ scale, float *__restrict__ y,
@@ -393,10 +410,20 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(Geom g, const uint32_t
 #pragma unroll
   for (int i = 0; i < NI; ++i)
     if (active) dma_to_lds(g.blob + g.off_code + code_off[i], region[i], code_rows[i] * 256, lane);
-  MvPrefetch<NI> pf;
-  if (!FP8 && active) mv_prefetch<NI>(pf, g, rb, c0, ncols, x, lane);
-  wait_all_loads();
-  __syncthreads();
+  MvPrefetch<NI, D> pf;
+  if (!FP8) {
+    if (active) mv_prefetch<NI, D>(pf, g, rb, c0, ncols, x, lane);
+    wait_copies_before<D * NI>(active);
+  } else {
+    wait_all_loads();
+  }
+  // Each wave has waited for its own copies into LDS; a bare barrier then
+  // makes all of them visible.  (__syncthreads() would add a fence that waits
+  // for every outstanding load, including the mantissa chunks meant to keep
+  // streaming in during the first groups.)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if (!active) return;
 
   const uint32_t lut = lds_addr(s_lut);
@@ -408,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void matvec_kernel(Geom g, const uint32_t
     Lane s[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) s[i] = Lane{lds_addr(region[i]) + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
-    mv_run<NI>(pf, s, c0, x, acc);
+    mv_run<NI, D>(pf, s, c0, x, acc);
   }
   const uint32_t kp = kspans_pad(g.n_kspans);
 #pragma unroll
@@ -602,15 +629,24 @@ int read_header(const void *header, nwc_header_t &h) {
   return nwc_check_header(&h);
 }
 
-template <bool FP8, int NI>
+template <bool FP8, int NI, int D>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
   const uint32_t waves = (g.n_rowblocks + NI - 1) / NI * g.n_kspans;
   const dim3 grid((waves + kWaves - 1) / kWaves), block(kThreads);
-  hipLaunchKernelGGL((matvec_kernel<FP8, NI>), grid, block, lds_bytes(g, NI), s, g,
+  hipLaunchKernelGGL((matvec_kernel<FP8, NI, D>), grid, block, lds_bytes(g, NI), s, g,
                      (const uint32_t *)(g.blob + g.off_items), (const uint16_t *)d_x, d_scale, d_y, partial);
   if (g.n_kspans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
                        g.n_kspans, g.n, d_scale, d_y);
+}
+
+// Mantissa prefetch ring depth (NWC_RING=1|2|4 overrides for experiments).
+int ring_depth() {
+  if (const char *e = getenv("NWC_RING")) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4) return v;
+  }
+  return 2;
 }
 
 }  // namespace
@@ -636,13 +672,14 @@ int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const fl
   const Geom g = make_geom(h, d_blob);
   hipStream_t s = (hipStream_t)stream;
   if (fp8) {
-    launch_matvec<true, 1>(g, s, d_x, d_scale, d_y, partial);
+    launch_matvec<true, 1, 1>(g, s, d_x, d_scale, d_y, partial);
   } else {
-    switch (matvec_chains(g)) {
-      case 4: launch_matvec<false, 4>(g, s, d_x, d_scale, d_y, partial); break;
-      case 2: launch_matvec<false, 2>(g, s, d_x, d_scale, d_y, partial); break;
-      default: launch_matvec<false, 1>(g, s, d_x, d_scale, d_y, partial); break;
-    }
+    const int ni = matvec_chains(g), d = ring_depth();
+    if (ni == 1 && d == 1) launch_matvec<false, 1, 1>(g, s, d_x, d_scale, d_y, partial);
+    else if (ni == 1 && d == 2) launch_matvec<false, 1, 2>(g, s, d_x, d_scale, d_y, partial);
+    else if (ni == 1) launch_matvec<false, 1, 4>(g, s, d_x, d_scale, d_y, partial);
+    else if (ni == 2) launch_matvec<false, 2, 2>(g, s, d_x, d_scale, d_y, partial);
+    else launch_matvec<false, 4, 2>(g, s, d_x, d_scale, d_y, partial);
   }
   return launched();
 }

@@ -183,7 +183,7 @@ def main():
                            "blob_MB": round(group[0]["blob_bytes"] / 1e6, 3),
                            "bits_per_weight_coded": round(group[0]["info"]["coded_bits"] / (n * k), 4),
                            "bits_per_weight_blob": round(group[0]["blob_bytes"] * 8 / (n * k), 4),
-                           "cols_per_item": group[0]["info"]["cols_per_item"]}
+                           "geometry": {f: group[0]["info"][f] for f in ("cols_per_lane", "rows_per_wave", "waves_per_group", "n_spans")}}
 
     bf16 = None
     if not args.no_bf16_baseline:

@@ -4,8 +4,8 @@
 // byte planes (raw mantissa byte, coded exponent/sign byte), per-matrix
 // frequency ranking, unary rank code with a raw sign bit and an escape; and
 // the "Qwen3-4B-NWC-fp8" model card for fp8 bytes coded whole.  The stream
-// layout (64-row work items, one lane column per row) is described in
-// nwc_format.h.
+// layout (work items of R rows x 64/R column slices, one lane per slice) is
+// described in nwc_format.h.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
@@ -134,62 +134,124 @@ void build_lut_fp8(const uint8_t *rank_to_sym, uint32_t *lut) {
   }
 }
 
-struct Plan {
-  int64_t n, k, ld;
-  int elem;
-  int C;
-  int64_t n_rb, n_ks, n_items;
-  std::vector<uint32_t> rows;  // code rows per item
+// Work-item geometry of one matrix (see nwc_format.h).
+struct Geo {
+  int C = 0, R = 0, S = 0, W = 0, n_spans = 0;
+  int64_t n_rg = 0, n_items = 0;
+  int64_t lane_cols() const { return n_rg * R * (int64_t)n_spans * W * S * C; }
 };
+
+Geo make_geo(int64_t n, int64_t k, int C, int R, int max_waves) {
+  Geo g;
+  g.C = C;
+  g.R = R;
+  g.S = NWC_LANES / R;
+  const int64_t waves_per_row = nwc_ceil_div(nwc_ceil_div(k, C), g.S);
+  g.n_spans = (int)nwc_ceil_div(waves_per_row, max_waves);
+  g.W = (int)nwc_ceil_div(waves_per_row, g.n_spans);
+  g.n_rg = nwc_ceil_div(n, R);
+  g.n_items = g.n_rg * g.n_spans * g.W;
+  return g;
+}
+
+// Automatic geometry.  Lanes decode C/2 (BF16) code pairs one after the
+// other, so C bounds a wave's decode latency; small matrices get C = 16 to
+// have enough waves.  Among the row counts R whose row group fits one
+// workgroup, pick the one that stores the fewest filler columns, then the
+// largest R (fewer, larger workgroups per decode table copy).  If that still
+// pads more than 3%, a wider C may pad less.
+Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req) {
+  std::vector<int> Cs, Rs;
+  if (C_req) Cs = {C_req};
+  else Cs = {n * k < ((int64_t)1 << 23) ? 16 : 32, 48, 64};
+  if (R_req) Rs = {R_req};
+  else Rs = {64, 32, 16, 8, 4, 2, 1};
+  Geo best;
+  int64_t best_cols = INT64_MAX;
+  for (int C : Cs) {
+    for (int R : Rs) {
+      const Geo g = make_geo(n, k, C, R, NWC_MAX_WAVES);
+      if (g.n_spans != 1 && !(R_req && C_req)) continue;
+      if (g.lane_cols() < best_cols) {
+        best = g;
+        best_cols = g.lane_cols();
+      }
+    }
+    if (best.C && (double)best_cols <= 1.03 * (double)n * (double)k) break;
+  }
+  if (!best.C) best = make_geo(n, k, Cs.back(), R_req ? R_req : 1, NWC_MAX_WAVES);  // k > 65536: several spans
+  return best;
+}
+
+// Lane L of item `item`: matrix row and first column (may lie past n / k).
+struct LaneSpan {
+  int64_t row, c0;
+};
+inline LaneSpan lane_span(const Geo &g, int64_t item, int L) {
+  const int64_t group = item / g.W, wave = item - group * g.W;
+  const int64_t rg = group / g.n_spans, span = group - rg * g.n_spans;
+  const int64_t q = (span * g.W + wave) * g.S + (L % g.S);
+  return {rg * g.R + L / g.S, q * g.C};
+}
 
 inline uint32_t symbol_index(const void *w, int elem, int64_t idx) {
   return elem == NWC_BF16 ? (uint32_t)(((const uint16_t *)w)[idx] >> 8) : (uint32_t)((const uint8_t *)w)[idx];
 }
 
-int auto_cols(int64_t n, int64_t k) {
-  const int64_t n_rb = nwc_ceil_div(n, NWC_LANES);
-  int C = NWC_MAX_COLS;
-  while (C > NWC_MIN_COLS && n_rb * nwc_ceil_div(k, C) < 2048) C /= 2;
-  return (int)std::min<int64_t>(C, nwc_round_up(k, 16));
+// Bits of one lane's stream: lead bits, its real codes, filler codes.
+uint64_t lane_bits(const void *w, int64_t n, int64_t k, int64_t ld, int elem, const CodeTable &tab,
+                   const Geo &g, const LaneSpan &ls) {
+  const uint64_t filler = elem == NWC_BF16 ? 2 : 5;
+  uint64_t bits = NWC_LEAD_BITS;
+  const int64_t real = ls.row < n ? std::max<int64_t>(0, std::min<int64_t>(k - ls.c0, g.C)) : 0;
+  const int64_t base = ls.row * ld + ls.c0;
+  for (int64_t c = 0; c < real; ++c) bits += tab.len[symbol_index(w, elem, base + c)];
+  return bits + filler * (uint64_t)(g.C - real);
 }
 
-// Longest lane stream (in 32-bit words) of every item for column count C.
-void plan_rows(const void *w, const CodeTable &tab, Plan &p) {
-  p.n_rb = nwc_ceil_div(p.n, NWC_LANES);
-  p.n_ks = nwc_ceil_div(p.k, p.C);
-  p.n_items = p.n_rb * p.n_ks;
-  p.rows.assign(p.n_items, 1);
-  parallel_for(p.n_rb, [&](int64_t b0, int64_t b1) {
-    for (int64_t rb = b0; rb < b1; ++rb)
-      for (int64_t ks = 0; ks < p.n_ks; ++ks) {
-        const int64_t c0 = ks * p.C, c1 = std::min<int64_t>(p.k, c0 + p.C);
-        uint64_t maxbits = NWC_LEAD_BITS;
-        for (int64_t L = 0; L < NWC_LANES; ++L) {
-          const int64_t row = rb * NWC_LANES + L;
-          if (row >= p.n) break;
-          uint64_t bits = NWC_LEAD_BITS;
-          const int64_t base = row * p.ld;
-          for (int64_t c = c0; c < c1; ++c) bits += tab.len[symbol_index(w, p.elem, base + c)];
-          maxbits = std::max(maxbits, bits);
-        }
-        p.rows[rb * p.n_ks + ks] = (uint32_t)nwc_ceil_div((int64_t)maxbits, 32);
-      }
+// Longest lane stream (in 32-bit words) of every item.
+std::vector<uint32_t> plan_rows(const void *w, int64_t n, int64_t k, int64_t ld, int elem, const CodeTable &tab,
+                                const Geo &g) {
+  std::vector<uint32_t> rows(g.n_items, 1);
+  parallel_for(g.n_items, [&](int64_t i0, int64_t i1) {
+    for (int64_t it = i0; it < i1; ++it) {
+      uint64_t maxbits = NWC_LEAD_BITS;
+      for (int L = 0; L < NWC_LANES; ++L)
+        maxbits = std::max(maxbits, lane_bits(w, n, k, ld, elem, tab, g, lane_span(g, it, L)));
+      rows[it] = (uint32_t)nwc_ceil_div((int64_t)maxbits, 32);
+    }
   });
+  return rows;
 }
 
-int64_t bound_bytes(int64_t n, int64_t k, int elem) {
-  // Worst case over every admissible column count: 16 code bits per weight.
+// Decoder LDS for one workgroup: staged code rows of W waves (+ guard rows),
+// the cross-wave row sums, the static decode table.
+int64_t lds_need(const Geo &g, uint32_t max_rows) {
+  return (int64_t)g.W * (max_rows + NWC_GUARD_ROWS) * 256 + (int64_t)g.W * g.R * 4 + NWC_LUT_BYTES;
+}
+
+int64_t bound_bytes(int64_t n, int64_t k, int elem, int C_req, int R_req) {
+  // Worst case over every admissible geometry: 16 code bits per weight.
   int64_t worst = 0;
   for (int C = 16; C <= NWC_MAX_COLS; C += 16) {
-    const int64_t n_rb = nwc_ceil_div(n, NWC_LANES), n_ks = nwc_ceil_div(k, C);
-    const int64_t items = n_rb * n_ks;
-    const int64_t k_pad = (n_ks - 1) * C + nwc_round_up(k - (n_ks - 1) * C, 16);
-    const int64_t mant = elem == NWC_BF16 ? n_rb * NWC_LANES * k_pad : 0;
-    const int64_t rows = nwc_ceil_div(NWC_LEAD_BITS + 16 * (int64_t)C, 32);
-    const int64_t code = items * rows * 256;
-    worst = std::max(worst, NWC_HEADER_BYTES + NWC_LUT_BYTES + nwc_round_up(items * 8, 256) + mant + code);
+    if (C_req && C != C_req) continue;
+    for (int R = 1; R <= NWC_LANES; R *= 2) {
+      if (R_req && R != R_req) continue;
+      for (int mw = NWC_MAX_WAVES; mw >= 1; --mw) {
+        const Geo g = make_geo(n, k, C, R, mw);
+        const int64_t mant = elem == NWC_BF16 ? g.n_items * NWC_LANES * C : 0;
+        const int64_t code = g.n_items * nwc_ceil_div(NWC_LEAD_BITS + 16 * (int64_t)C, 32) * 256;
+        worst = std::max(worst, NWC_HEADER_BYTES + NWC_LUT_BYTES + nwc_round_up(g.n_items * 8, 256) + mant + code);
+      }
+    }
   }
   return worst;
+}
+
+bool valid_geometry_request(int C, int R) {
+  if (C != 0 && (C < 16 || C > NWC_MAX_COLS || C % 16)) return false;
+  if (R != 0 && (R < 1 || R > NWC_LANES || (R & (R - 1)))) return false;
+  return true;
 }
 
 }  // namespace
@@ -211,22 +273,20 @@ const char *nwc_status_string(int s) {
   }
 }
 
-int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_item, int64_t *max_bytes) {
+int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_lane, int rows_per_wave, int64_t *max_bytes) {
   if (!max_bytes) return NWC_ERR_ARG;
   if (elem != NWC_BF16 && elem != NWC_FP8_E4M3) return NWC_ERR_ARG;
-  if (cols_per_item != 0 && (cols_per_item < 16 || cols_per_item > NWC_MAX_COLS || cols_per_item % 16))
-    return NWC_ERR_ARG;
+  if (!valid_geometry_request(cols_per_lane, rows_per_wave)) return NWC_ERR_ARG;
   if (n <= 0 || k <= 0 || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return NWC_ERR_SHAPE;
-  *max_bytes = bound_bytes(n, k, elem);
+  *max_bytes = bound_bytes(n, k, elem, cols_per_lane, rows_per_wave);
   return NWC_OK;
 }
 
-int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_item, void *blob,
-               int64_t blob_cap, int64_t *blob_size) {
+int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_lane, int rows_per_wave,
+               void *blob, int64_t blob_cap, int64_t *blob_size) {
   if (!w || !blob || !blob_size) return NWC_ERR_ARG;
   if (elem != NWC_BF16 && elem != NWC_FP8_E4M3) return NWC_ERR_ARG;
-  if (cols_per_item != 0 && (cols_per_item < 16 || cols_per_item > NWC_MAX_COLS || cols_per_item % 16))
-    return NWC_ERR_ARG;
+  if (!valid_geometry_request(cols_per_lane, rows_per_wave)) return NWC_ERR_ARG;
   if (n <= 0 || k <= 0 || ld < k || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return NWC_ERR_SHAPE;
 
   // 1. histogram of the ranked symbol over the real weights
@@ -265,15 +325,17 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   else
     fp8_codes(sym_to_rank, tab);
 
-  // 3. work-item geometry; shrink the column span if a stream would not fit
-  Plan p{n, k, ld, elem, cols_per_item ? cols_per_item : auto_cols(n, k), 0, 0, 0, {}};
-  p.C = (int)std::min<int64_t>(p.C, nwc_round_up(k, 16));
-  for (;;) {
-    plan_rows(w, tab, p);
-    const uint32_t mx = *std::max_element(p.rows.begin(), p.rows.end());
-    if (mx <= NWC_ROWS_CAP) break;
-    if (p.C <= NWC_MIN_COLS) return NWC_ERR_UNSUPPORTED;  // cannot happen: 64 cols need <= 33 rows
-    p.C = std::max(NWC_MIN_COLS, p.C / 2);
+  // 3. work-item geometry; fewer waves per workgroup (more column spans) if
+  // the staged code rows of a workgroup would not fit the decoder's LDS.
+  Geo g = auto_geo(n, k, cols_per_lane, rows_per_wave);
+  std::vector<uint32_t> rows;
+  for (int mw = NWC_MAX_WAVES;; --mw) {
+    rows = plan_rows(w, n, k, ld, elem, tab, g);
+    const uint32_t mx = *std::max_element(rows.begin(), rows.end());
+    if (mx > NWC_ROWS_CAP) return NWC_ERR_UNSUPPORTED;  // cannot happen: C <= 64 needs <= 33 rows
+    if (lds_need(g, mx) <= NWC_LDS_BUDGET) break;
+    if (g.W == 1) return NWC_ERR_UNSUPPORTED;  // cannot happen: one wave needs < 26 KiB
+    g = make_geo(n, k, g.C, g.R, std::min(mw - 1, g.W - 1));
   }
 
   // 4. layout
@@ -283,26 +345,26 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   hd.header_bytes = NWC_HEADER_BYTES;
   hd.n = n;
   hd.k = k;
-  hd.cols_per_item = (uint32_t)p.C;
-  hd.n_rowblocks = (uint32_t)p.n_rb;
-  hd.n_kspans = (uint32_t)p.n_ks;
-  hd.n_items = (uint32_t)p.n_items;
-  hd.max_rows = *std::max_element(p.rows.begin(), p.rows.end());
+  hd.cols_per_lane = (uint32_t)g.C;
+  hd.rows_per_wave = (uint32_t)g.R;
+  hd.waves_per_group = (uint32_t)g.W;
+  hd.n_spans = (uint32_t)g.n_spans;
+  hd.n_rowgroups = (uint32_t)g.n_rg;
+  hd.n_items = (uint32_t)g.n_items;
+  hd.max_rows = *std::max_element(rows.begin(), rows.end());
   hd.escape_r = NWC_ESCAPE_R;
-  hd.last_cols = (uint32_t)(k - (p.n_ks - 1) * p.C);
-  hd.k_pad = (uint32_t)((p.n_ks - 1) * p.C + nwc_round_up(hd.last_cols, 16));
   hd.off_lut = NWC_HEADER_BYTES;
   hd.off_items = hd.off_lut + NWC_LUT_BYTES;
-  hd.off_mant = hd.off_items + (uint64_t)nwc_round_up(p.n_items * 8, 256);
-  hd.mant_bytes = elem == NWC_BF16 ? (uint64_t)p.n_rb * NWC_LANES * hd.k_pad : 0;
+  hd.off_mant = hd.off_items + (uint64_t)nwc_round_up(g.n_items * 8, 256);
+  hd.mant_bytes = elem == NWC_BF16 ? (uint64_t)g.n_items * NWC_LANES * g.C : 0;
   hd.off_code = hd.off_mant + hd.mant_bytes;
-  std::vector<uint32_t> code_off(p.n_items);
+  std::vector<uint32_t> code_off(g.n_items);
   uint64_t code_bytes = 0;
-  for (int64_t i = 0; i < p.n_items; ++i) {
+  for (int64_t i = 0; i < g.n_items; ++i) {
     code_off[i] = (uint32_t)code_bytes;
-    code_bytes += (uint64_t)p.rows[i] * 256;
+    code_bytes += (uint64_t)rows[i] * 256;
+    if (code_bytes > 0xFFFFFFFFull) return NWC_ERR_SHAPE;  // item offsets are 32-bit
   }
-  if (code_bytes > 0xFFFFFFFFull) return NWC_ERR_SHAPE;  // item offsets are 32-bit
   hd.code_bytes = code_bytes;
   hd.total_bytes = hd.off_code + code_bytes;
   if ((int64_t)hd.total_bytes > blob_cap) return NWC_ERR_CAPACITY;
@@ -324,46 +386,43 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   else
     build_lut_fp8(hd.rank_to_sym, lut);
   uint32_t *items = (uint32_t *)(out + hd.off_items);
-  for (int64_t i = 0; i < p.n_items; ++i) {
+  for (int64_t i = 0; i < g.n_items; ++i) {
     items[2 * i] = code_off[i];
-    items[2 * i + 1] = p.rows[i];
+    items[2 * i + 1] = rows[i];
   }
 
-  // 7. code and mantissa planes, one row block per task
-  parallel_for(p.n_rb, [&](int64_t b0, int64_t b1) {
-    for (int64_t rb = b0; rb < b1; ++rb)
-      for (int64_t ks = 0; ks < p.n_ks; ++ks) {
-        const int64_t item = rb * p.n_ks + ks;
-        const uint32_t rows = p.rows[item];
-        uint32_t *code = (uint32_t *)(out + hd.off_code + code_off[item]);
-        memset(code, 0, (size_t)rows * 256);
-        const int64_t c0 = ks * p.C, c1 = std::min<int64_t>(k, c0 + p.C), nc = c1 - c0;
-        uint8_t *mant = nullptr;
-        if (elem == NWC_BF16) {
-          mant = out + hd.off_mant + (uint64_t)rb * NWC_LANES * hd.k_pad + (uint64_t)NWC_LANES * c0;
-          memset(mant, 0, (size_t)NWC_LANES * nwc_round_up(nc, 16));
-        }
-        for (int64_t L = 0; L < NWC_LANES; ++L) {
-          const int64_t row = rb * NWC_LANES + L;
-          if (row >= n) break;
-          uint64_t acc = 0;
-          uint32_t nbits = NWC_LEAD_BITS, word = 0;
-          for (int64_t c = 0; c < nc; ++c) {
-            const int64_t idx = row * ld + c0 + c;
-            const uint32_t sym = symbol_index(w, elem, idx);
-            acc |= (uint64_t)tab.val[sym] << nbits;
-            nbits += tab.len[sym];
-            if (nbits >= 32) {
-              code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
-              acc >>= 32;
-              nbits -= 32;
-              ++word;
-            }
-            if (mant) mant[((c >> 4) * NWC_LANES + L) * 16 + (c & 15)] = (uint8_t)((const uint16_t *)w)[idx];
-          }
-          if (nbits) code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
-        }
+  // 7. code and mantissa planes, one item per task (fillers stay zero)
+  parallel_for(g.n_items, [&](int64_t i0, int64_t i1) {
+    for (int64_t it = i0; it < i1; ++it) {
+      uint32_t *code = (uint32_t *)(out + hd.off_code + code_off[it]);
+      memset(code, 0, (size_t)rows[it] * 256);
+      uint8_t *mant = nullptr;
+      if (elem == NWC_BF16) {
+        mant = out + hd.off_mant + (uint64_t)it * NWC_LANES * g.C;
+        memset(mant, 0, (size_t)NWC_LANES * g.C);
       }
+      for (int L = 0; L < NWC_LANES; ++L) {
+        const LaneSpan ls = lane_span(g, it, L);
+        if (ls.row >= n || ls.c0 >= k) continue;
+        const int64_t nc = std::min<int64_t>(k - ls.c0, g.C);
+        uint64_t acc = 0;
+        uint32_t nbits = NWC_LEAD_BITS, word = 0;
+        for (int64_t c = 0; c < nc; ++c) {
+          const int64_t idx = ls.row * ld + ls.c0 + c;
+          const uint32_t sym = symbol_index(w, elem, idx);
+          acc |= (uint64_t)tab.val[sym] << nbits;
+          nbits += tab.len[sym];
+          if (nbits >= 32) {
+            code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
+            acc >>= 32;
+            nbits -= 32;
+            ++word;
+          }
+          if (mant) mant[((c >> 4) * NWC_LANES + L) * 16 + (c & 15)] = (uint8_t)((const uint16_t *)w)[idx];
+        }
+        if (nbits) code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
+      }
+    }
   });
   *blob_size = (int64_t)hd.total_bytes;
   return NWC_OK;
@@ -380,7 +439,10 @@ int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info) {
   info->n = h.n;
   info->k = h.k;
   info->elem = (int32_t)h.elem;
-  info->cols_per_item = (int32_t)h.cols_per_item;
+  info->cols_per_lane = (int32_t)h.cols_per_lane;
+  info->rows_per_wave = (int32_t)h.rows_per_wave;
+  info->waves_per_group = (int32_t)h.waves_per_group;
+  info->n_spans = (int32_t)h.n_spans;
   info->n_items = (int32_t)h.n_items;
   info->max_rows = (int32_t)h.max_rows;
   info->coded_bits = h.coded_bits;
@@ -398,12 +460,12 @@ int nwc_workspace_size(const void *header, int64_t *bytes) {
   memcpy(&h, header, sizeof h);
   const int st = nwc_check_header(&h);
   if (st != NWC_OK) return st;
-  if (h.n_kspans == 1) {
+  if (h.n_spans == 1) {
     *bytes = 0;
     return NWC_OK;
   }
   // fp32 partial sums [row][column span padded to a multiple of 4]
-  *bytes = nwc_round_up((int64_t)h.n_rowblocks * NWC_LANES * nwc_round_up(h.n_kspans, 4) * 4, 256);
+  *bytes = nwc_round_up((int64_t)h.n_rowgroups * h.rows_per_wave * nwc_round_up(h.n_spans, 4) * 4, 256);
   return NWC_OK;
 }
 

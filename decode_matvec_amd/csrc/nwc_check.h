@@ -9,6 +9,13 @@
 static inline int64_t nwc_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline int64_t nwc_round_up(int64_t a, int64_t b) { return nwc_ceil_div(a, b) * b; }
 
+// Decoder LDS of one workgroup for this header: W staged code regions (with
+// guard rows), the cross-wave row sums, the static decode table.
+static inline int64_t nwc_lds_bytes(const nwc_header_t *h) {
+  return (int64_t)h->waves_per_group * (h->max_rows + NWC_GUARD_ROWS) * 256 +
+         (int64_t)h->waves_per_group * h->rows_per_wave * 4 + NWC_LUT_BYTES;
+}
+
 // Returns NWC_OK if `h` is a structurally valid header of this format version.
 static inline int nwc_check_header(const nwc_header_t *h) {
   if (!h) return NWC_ERR_ARG;
@@ -16,16 +23,18 @@ static inline int nwc_check_header(const nwc_header_t *h) {
     return NWC_ERR_FORMAT;
   if (h->elem != NWC_BF16 && h->elem != NWC_FP8_E4M3) return NWC_ERR_FORMAT;
   if (h->n <= 0 || h->k <= 0 || h->n > (int64_t)1 << 31 || h->k > (int64_t)1 << 31) return NWC_ERR_FORMAT;
-  const int64_t C = h->cols_per_item;
+  const int64_t C = h->cols_per_lane, R = h->rows_per_wave, W = h->waves_per_group, sp = h->n_spans;
   if (C < 16 || C > NWC_MAX_COLS || C % 16) return NWC_ERR_FORMAT;
-  if (h->n_rowblocks != nwc_ceil_div(h->n, NWC_LANES)) return NWC_ERR_FORMAT;
-  if (h->n_kspans != nwc_ceil_div(h->k, C)) return NWC_ERR_FORMAT;
-  if ((int64_t)h->n_items != (int64_t)h->n_rowblocks * h->n_kspans) return NWC_ERR_FORMAT;
-  if (h->last_cols != h->k - (int64_t)(h->n_kspans - 1) * C) return NWC_ERR_FORMAT;
-  if (h->k_pad != (int64_t)(h->n_kspans - 1) * C + nwc_round_up(h->last_cols, 16)) return NWC_ERR_FORMAT;
+  if (R < 1 || R > NWC_LANES || (R & (R - 1))) return NWC_ERR_FORMAT;
+  if (W < 1 || W > NWC_MAX_WAVES || sp < 1) return NWC_ERR_FORMAT;
+  const int64_t waves_per_row = nwc_ceil_div(nwc_ceil_div(h->k, C), NWC_LANES / R);
+  if (sp * W < waves_per_row || sp * (W - 1) >= waves_per_row) return NWC_ERR_FORMAT;
+  if (h->n_rowgroups != nwc_ceil_div(h->n, R)) return NWC_ERR_FORMAT;
+  if ((int64_t)h->n_items != (int64_t)h->n_rowgroups * sp * W) return NWC_ERR_FORMAT;
   if (h->max_rows < 1 || h->max_rows > NWC_ROWS_CAP || h->escape_r != NWC_ESCAPE_R) return NWC_ERR_FORMAT;
+  if (nwc_lds_bytes(h) > NWC_LDS_BUDGET) return NWC_ERR_FORMAT;
   const uint64_t items_bytes = (uint64_t)nwc_round_up((int64_t)h->n_items * 8, 256);
-  const uint64_t mant = h->elem == NWC_BF16 ? (uint64_t)h->n_rowblocks * NWC_LANES * h->k_pad : 0;
+  const uint64_t mant = h->elem == NWC_BF16 ? (uint64_t)h->n_items * NWC_LANES * C : 0;
   if (h->off_lut != NWC_HEADER_BYTES || h->off_items != h->off_lut + NWC_LUT_BYTES ||
       h->off_mant != h->off_items + items_bytes || h->mant_bytes != mant ||
       h->off_code != h->off_mant + h->mant_bytes || h->off_code % 256 ||

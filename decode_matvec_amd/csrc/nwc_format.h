@@ -12,23 +12,37 @@
 // Layout (little endian, every section 256-byte aligned):
 //   header     256 B    nwc_header_t
 //   lut        16 KiB   4096 x u32 decode table indexed by a 12-bit peek
-//   items      8 B per item: {u32 code_offset, u32 code_rows}
-//   mant       BF16 only: raw mantissa bytes
+//   items      8 B per work item: {u32 code byte offset, u32 code rows}
+//   mant       BF16 only: raw mantissa bytes, 64*C bytes per item
 //   code       per item: code_rows x 64 lane columns of u32
 //
-// Work item = 64 matrix rows (one per lane of a wave) x cols_per_item columns.
-// Items are numbered item = rowblock * n_kspans + kspan.
+// Geometry.  A work item is what one wave decodes: R rows (R = rows_per_wave,
+// a power of two) times S = 64/R slices per row, a slice being C consecutive
+// columns (C = cols_per_lane, a multiple of 16).  Lane L of an item holds row
+// L / S of its row group and slice L % S, so the S lanes of a row are
+// adjacent.  A row's slices are numbered q = 0, 1, ... (columns [qC, qC+C)).
+// A group of W consecutive items (W = waves_per_group, one workgroup) covers
+// S*W consecutive slices of the same R rows; n_spans groups cover a whole row
+// group (one in every shape with K <= 16*S*C).
+//   item = (row_group * n_spans + span) * W + wave
+//   lane L: row = row_group*R + L/S, slice q = (span*W + wave)*S + L%S
+//
+// Fillers.  Columns at or past K and rows at or past N are fillers: zero code
+// bits, which decode as rank 0 with sign 0, and zero mantissa bytes.  A filler
+// therefore decodes to a finite value (BF16 exponent field 2*symbol <= 254;
+// fp8 mantissa 0 is never NaN) and adds exactly zero against the zero
+// activation the kernel uses past column K.
 //
 // Code plane of an item: lane L owns column L of a (code_rows x 64) u32 array,
 // i.e. its stream's word w lives at u32 index w*64 + L.  A lane's stream starts
-// with 2 zero bits, then the codes of its row's weights in column order, bits
-// least-significant first.  Columns are zero-padded to the item's longest
-// stream.  Rows past N have empty (all-zero) streams.
+// with 2 zero bits, then the codes of its C columns (fillers included) in
+// column order, bits least-significant first; code_rows covers the longest
+// lane, shorter lanes are zero-padded.  Decoders keep two zero rows after the
+// item's rows so a 64-bit read at the last code stays defined.
 //
 // Mantissa plane of an item (BF16): lane L's mantissa bytes in column order,
 // in 16-byte chunks; chunk j of lane L at byte (j*64 + L)*16 of the item's
-// region.  Item (rb, ks) region starts at rb*64*k_pad + 64*ks*cols_per_item,
-// where k_pad sums each kspan's column count rounded up to 16.
+// 64*C-byte block, so a wave's load of chunk j is one contiguous KiB.
 //
 // Decode table (BF16): entry for peek p (12 stream bits, first bit = bit 0):
 //   two complete codes A, B within the 12 bits:
@@ -41,17 +55,18 @@
 #include <stdint.h>
 
 #define NWC_MAGIC 0x3143574Eu /* "NWC1" */
-#define NWC_FORMAT_VERSION 1u
+#define NWC_FORMAT_VERSION 2u
 #define NWC_HEADER_BYTES 256
 #define NWC_LANES 64
 #define NWC_LUT_ENTRIES 4096
 #define NWC_LUT_BYTES (NWC_LUT_ENTRIES * 4)
 #define NWC_ESCAPE_R 8
 #define NWC_LEAD_BITS 2
-#define NWC_ROWS_CAP 40
-#define NWC_MAX_COLS 256
-#define NWC_MIN_COLS 64
+#define NWC_MAX_COLS 64     /* cols_per_lane: multiple of 16 in [16, 64] */
+#define NWC_MAX_WAVES 16    /* waves per workgroup (1024 threads) */
+#define NWC_ROWS_CAP 40     /* longest lane stream: 2 + 16*64 bits < 33 words */
 #define NWC_GUARD_ROWS 2
+#define NWC_LDS_BUDGET (64 * 1024) /* decoder LDS per workgroup the encoder plans for */
 
 #ifdef __cplusplus
 extern "C" {
@@ -60,23 +75,23 @@ extern "C" {
 typedef struct nwc_header_t {
   uint32_t magic;
   uint32_t version;
-  uint32_t elem;           /* 0 = BF16, 1 = fp8 e4m3fn */
+  uint32_t elem;             /* 0 = BF16, 1 = fp8 e4m3fn */
   uint32_t header_bytes;
-  int64_t n;               /* rows (output features) */
-  int64_t k;               /* columns (input features) */
-  uint32_t cols_per_item;  /* multiple of 16, 16..256 */
-  uint32_t n_rowblocks;    /* ceil(n / 64) */
-  uint32_t n_kspans;       /* ceil(k / cols_per_item) */
-  uint32_t n_items;        /* n_rowblocks * n_kspans */
-  uint32_t max_rows;       /* largest code_rows of any item */
-  uint32_t escape_r;       /* 8 */
-  uint32_t last_cols;      /* columns of the last kspan */
-  uint32_t k_pad;          /* sum over kspans of round_up(cols, 16) */
-  uint64_t coded_bits;     /* code bits of the real weights (+ 8 per BF16 weight) */
+  int64_t n;                 /* rows (output features) */
+  int64_t k;                 /* columns (input features) */
+  uint32_t cols_per_lane;    /* C */
+  uint32_t rows_per_wave;    /* R, power of two in [1, 64] */
+  uint32_t waves_per_group;  /* W, 1..16 */
+  uint32_t n_spans;          /* workgroups per row group */
+  uint32_t n_rowgroups;      /* ceil(n / R) */
+  uint32_t n_items;          /* n_rowgroups * n_spans * W */
+  uint32_t max_rows;         /* largest code_rows of any item */
+  uint32_t escape_r;         /* 8 */
+  uint64_t coded_bits;       /* code bits of the real weights (+ 8 per BF16 weight) */
   uint64_t off_lut, off_items, off_mant, off_code;
   uint64_t total_bytes;
   uint64_t code_bytes, mant_bytes;
-  uint8_t rank_to_sym[128]; /* 128 BF16 symbols, or 16 fp8 exponent fields */
+  uint8_t rank_to_sym[128];  /* 128 BF16 symbols, or 16 fp8 exponent fields */
 } nwc_header_t;
 
 #ifdef __cplusplus

@@ -35,7 +35,9 @@ class NWCError(RuntimeError):
 
 class NWCInfo(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("elem", ctypes.c_int32),
-                ("cols_per_item", ctypes.c_int32), ("n_items", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+                ("cols_per_lane", ctypes.c_int32), ("rows_per_wave", ctypes.c_int32),
+                ("waves_per_group", ctypes.c_int32), ("n_spans", ctypes.c_int32), ("n_items", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("coded_bits", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
                 ("code_bytes", ctypes.c_uint64), ("mant_bytes", ctypes.c_uint64),
                 ("table_bytes", ctypes.c_uint64), ("rank_to_sym", ctypes.c_uint8 * 128)]
@@ -49,8 +51,8 @@ def _load():
     sig = {
         "nwc_version": ([], ci),
         "nwc_status_string": ([ci], ctypes.c_char_p),
-        "nwc_encode_bound": ([i64, i64, ci, ci, ctypes.POINTER(i64)], ci),
-        "nwc_encode": ([vp, i64, i64, i64, ci, ci, vp, i64, ctypes.POINTER(i64)], ci),
+        "nwc_encode_bound": ([i64, i64, ci, ci, ci, ctypes.POINTER(i64)], ci),
+        "nwc_encode": ([vp, i64, i64, i64, ci, ci, ci, vp, i64, ctypes.POINTER(i64)], ci),
         "nwc_blob_info": ([vp, i64, ctypes.POINTER(NWCInfo)], ci),
         "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
         "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
@@ -84,14 +86,16 @@ def _host_ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def encode_bound(n: int, k: int, elem: int = NWC_BF16, cols_per_item: int = 0) -> int:
+def encode_bound(n: int, k: int, elem: int = NWC_BF16, cols_per_lane: int = 0, rows_per_wave: int = 0) -> int:
     out = ctypes.c_int64()
-    _check("nwc_encode_bound", lib.nwc_encode_bound(n, k, elem, cols_per_item, ctypes.byref(out)))
+    _check("nwc_encode_bound", lib.nwc_encode_bound(n, k, elem, cols_per_lane, rows_per_wave, ctypes.byref(out)))
     return out.value
 
 
-def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_item: int = 0) -> np.ndarray:
-    """Encode a host matrix (uint16 BF16 patterns or uint8 fp8 bytes) -> uint8 blob."""
+def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_lane: int = 0, rows_per_wave: int = 0) -> np.ndarray:
+    """Encode a host matrix (uint16 BF16 patterns or uint8 fp8 bytes) -> uint8 blob.
+
+    cols_per_lane / rows_per_wave: 0 lets the library choose the work-item geometry."""
     want = np.uint16 if elem == NWC_BF16 else np.uint8
     if w.dtype != want or w.ndim != 2:
         raise TypeError(f"expected a 2-D {np.dtype(want).name} array, got {w.dtype} {w.shape}")
@@ -99,11 +103,11 @@ def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_item: int = 0) -> np.nd
         w = np.ascontiguousarray(w)
     n, k = w.shape
     ld = w.strides[0] // w.itemsize
-    cap = encode_bound(n, k, elem, cols_per_item)
+    cap = encode_bound(n, k, elem, cols_per_lane, rows_per_wave)
     blob = np.empty(cap, dtype=np.uint8)
     size = ctypes.c_int64()
-    _check("nwc_encode", lib.nwc_encode(_host_ptr(w), n, k, ld, elem, cols_per_item, _host_ptr(blob), cap,
-                                        ctypes.byref(size)))
+    _check("nwc_encode", lib.nwc_encode(_host_ptr(w), n, k, ld, elem, cols_per_lane, rows_per_wave, _host_ptr(blob),
+                                        cap, ctypes.byref(size)))
     return blob[:size.value].copy()
 
 

@@ -56,9 +56,13 @@ typedef enum nwc_elem {
 typedef struct nwc_info {
   int64_t n, k;
   int32_t elem;
-  int32_t cols_per_item;   /* columns per work item (per-lane stream length) */
-  int32_t n_items;         /* 64-row x cols_per_item work items */
+  int32_t cols_per_lane;   /* C: columns of one lane's stream (one row slice) */
+  int32_t rows_per_wave;   /* R: rows of a work item; 64/R lanes share a row */
+  int32_t waves_per_group; /* W: work items (waves) per workgroup */
+  int32_t n_spans;         /* workgroups along one row (1 unless k > 16*64*C/R) */
+  int32_t n_items;         /* work items (one wave each) */
   int32_t max_rows;        /* longest item code column, in 32-bit words */
+  int32_t reserved;
   uint64_t coded_bits;     /* sum of codeword lengths of the real weights, plus
                               8 raw mantissa bits per BF16 weight */
   uint64_t total_bytes;    /* whole blob */
@@ -74,9 +78,9 @@ int nwc_version(void);
 /* Static description of a status code. */
 const char *nwc_status_string(int status);
 
-/* Upper bound of the blob size nwc_encode can produce for an n x k matrix.
- * cols_per_item: 0 (automatic) or a multiple of 16 in [64, 256]. */
-int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_item, int64_t *max_bytes);
+/* Upper bound of the blob size nwc_encode can produce for an n x k matrix
+ * with the same geometry request (see nwc_encode). */
+int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_lane, int rows_per_wave, int64_t *max_bytes);
 
 /* Host-side encoder ("How it works": byte planes, per-matrix frequency rank
  * table, unary rank code + raw sign + escape; model card: fp8 bytes coded whole).
@@ -84,21 +88,23 @@ int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_item, int64_t 
  *            patterns for NWC_BF16, uint8 e4m3fn bytes for NWC_FP8_E4M3.
  *   blob     caller-owned host buffer of blob_cap bytes (see nwc_encode_bound);
  *            on success the blob occupies *blob_size bytes from its start.
- *   cols_per_item: 0 = choose from the shape; else a multiple of 16 in
- *            [64, 256] (reduced automatically if a work item's longest code
- *            column would exceed the decoder's staging capacity).
+ *   cols_per_lane: 0 = choose from the shape; else 16, 32, 48 or 64 columns
+ *            per lane stream (a lane's decode chain is cols_per_lane/2 steps).
+ *   rows_per_wave: 0 = choose from the shape; else a power of two in [1, 64]:
+ *            the rows one wave decodes, each split over 64/rows_per_wave lanes.
  * Any BF16 pattern (NaN payloads, infinities, zeros, subnormals) and any fp8
  * byte is encoded losslessly.  Uses up to hardware_concurrency host threads. */
-int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_item,
-               void *blob, int64_t blob_cap, int64_t *blob_size);
+int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_lane,
+               int rows_per_wave, void *blob, int64_t blob_cap, int64_t *blob_size);
 
 /* Validate a blob header (host pointer, at least NWC_HEADER_BYTES) and
  * describe it.  blob_bytes: bytes available at `blob` (>= header bytes). */
 int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info);
 
-/* Device workspace bytes nwc_matvec needs for this blob (0 if the matrix has
- * a single column span): fp32 partial sums of each row per column span.  Its
- * contents need no initialisation and are overwritten by every call. */
+/* Device workspace bytes nwc_matvec needs for this blob: 0 unless a row is
+ * split over several workgroups (n_spans > 1, only for k > 16*64*C/R), then
+ * fp32 partial sums of each row per span.  Its contents need no
+ * initialisation and are overwritten by every call. */
 int nwc_workspace_size(const void *header, int64_t *bytes);
 
 /* Fused decode + matvec ("Fused kernel": weights decoded in registers, fp32
@@ -109,9 +115,10 @@ int nwc_workspace_size(const void *header, int64_t *bytes);
  *   d_ws     device workspace of ws_bytes >= nwc_workspace_size, 256-byte
  *            aligned; may be NULL when the size is 0.  Concurrent calls need
  *            distinct workspaces.
- * Enqueues the fused kernel and, for matrices with more than one column span,
- * a second small kernel that sums the spans' partials.  The summation order
- * is fixed, so repeated calls give identical bits. */
+ * One kernel: a workgroup decodes whole rows and sums them across its lanes
+ * and waves.  Only when n_spans > 1 is a second small kernel enqueued to sum
+ * the spans' partials.  The summation order is fixed, so repeated calls give
+ * identical bits. */
 int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const float *d_scale,
                float *d_y, void *d_ws, int64_t ws_bytes, void *stream);
 

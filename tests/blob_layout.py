@@ -10,9 +10,9 @@ import numpy as np
 import oracle as O
 
 HDR = np.dtype([("magic", "<u4"), ("version", "<u4"), ("elem", "<u4"), ("header_bytes", "<u4"),
-                ("n", "<i8"), ("k", "<i8"), ("cols_per_item", "<u4"), ("n_rowblocks", "<u4"),
-                ("n_kspans", "<u4"), ("n_items", "<u4"), ("max_rows", "<u4"), ("escape_r", "<u4"),
-                ("last_cols", "<u4"), ("k_pad", "<u4"), ("coded_bits", "<u8"), ("off_lut", "<u8"),
+                ("n", "<i8"), ("k", "<i8"), ("cols_per_lane", "<u4"), ("rows_per_wave", "<u4"),
+                ("waves_per_group", "<u4"), ("n_spans", "<u4"), ("n_rowgroups", "<u4"), ("n_items", "<u4"),
+                ("max_rows", "<u4"), ("escape_r", "<u4"), ("coded_bits", "<u8"), ("off_lut", "<u8"),
                 ("off_items", "<u8"), ("off_mant", "<u8"), ("off_code", "<u8"), ("total_bytes", "<u8"),
                 ("code_bytes", "<u8"), ("mant_bytes", "<u8"), ("rank_to_sym", "u1", (128,))])
 assert HDR.itemsize == 256
@@ -23,6 +23,16 @@ def header(blob: np.ndarray) -> dict:
     return {name: (h[name] if name == "rank_to_sym" else int(h[name])) for name in HDR.names}
 
 
+def lane_place(h, item, lane):
+    """(row, first column) of lane `lane` of work item `item`."""
+    R, W, sp = h["rows_per_wave"], h["waves_per_group"], h["n_spans"]
+    S, C = 64 // R, h["cols_per_lane"]
+    group, wave = divmod(item, W)
+    rg, span = divmod(group, sp)
+    q = (span * W + wave) * S + lane % S
+    return rg * R + lane // S, q * C
+
+
 def lane_bits(blob, h, item, lane):
     off, rows = np.frombuffer(blob[h["off_items"] + 8 * item: h["off_items"] + 8 * item + 8].tobytes(), "<u4")
     base = h["off_code"] + int(off)
@@ -30,46 +40,57 @@ def lane_bits(blob, h, item, lane):
     return np.unpackbits(words.astype("<u4").view(np.uint8), bitorder="little")
 
 
+def mant_byte(blob, h, item, lane, c):
+    return blob[h["off_mant"] + item * 64 * h["cols_per_lane"] + ((c >> 4) * 64 + lane) * 16 + (c & 15)]
+
+
+def _parse_fp8(bits, pos, r2s):
+    r = 0
+    while r < 8 and bits[pos + r] == 1:
+        r += 1
+    if r < 8:
+        s = bits[pos + r + 1]
+        M = bits[pos + r + 2] | bits[pos + r + 3] << 1 | bits[pos + r + 4] << 2
+        return (s << 7) | (int(r2s[r]) << 3) | M, pos + r + 5
+    s = bits[pos + 8]
+    E = sum(bits[pos + 9 + i] << i for i in range(4))
+    M = sum(bits[pos + 13 + i] << i for i in range(3))
+    return (s << 7) | (E << 3) | M, pos + 16
+
+
 def decode_blob(blob: np.ndarray) -> np.ndarray:
-    """Whole matrix from a library blob (uint16 BF16 patterns or uint8 fp8 bytes)."""
+    """Whole matrix from a library blob (uint16 BF16 patterns or uint8 fp8 bytes).
+
+    Also asserts the filler convention: every lane stream starts with two zero
+    bits, and stream bits past a lane's real columns, and mantissa bytes of
+    filler columns, are zero."""
     h = header(blob)
-    n, k, C = h["n"], h["k"], h["cols_per_item"]
+    n, k, C = h["n"], h["k"], h["cols_per_lane"]
     fp8 = h["elem"] == 1
     r2s = np.array(h["rank_to_sym"][: 16 if fp8 else 128], dtype=np.int64)
     out = np.zeros((n, k), dtype=np.uint8 if fp8 else np.uint16)
-    for rb in range(h["n_rowblocks"]):
-        for ks in range(h["n_kspans"]):
-            item = rb * h["n_kspans"] + ks
-            c0 = ks * C
-            nc = h["last_cols"] if ks == h["n_kspans"] - 1 else C
-            mbase = h["off_mant"] + rb * 64 * h["k_pad"] + 64 * c0
-            for L in range(64):
-                row = rb * 64 + L
-                if row >= n:
-                    break
-                bits = list(lane_bits(blob, h, item, L)) + [0] * 32
-                assert bits[0] == 0 and bits[1] == 0
-                pos = 2
-                for c in range(nc):
-                    if fp8:
-                        r = 0
-                        while r < 8 and bits[pos + r] == 1:
-                            r += 1
-                        if r < 8:
-                            s = bits[pos + r + 1]
-                            M = bits[pos + r + 2] | bits[pos + r + 3] << 1 | bits[pos + r + 4] << 2
-                            E = int(r2s[r])
-                            pos += r + 5
-                        else:
-                            s = bits[pos + 8]
-                            E = sum(bits[pos + 9 + i] << i for i in range(4))
-                            M = sum(bits[pos + 13 + i] << i for i in range(3))
-                            pos += 16
-                        out[row, c0 + c] = (s << 7) | (E << 3) | M
-                    else:
-                        s, e, pos = O.parse_one_bf16(bits, pos, r2s)
-                        m = blob[mbase + ((c >> 4) * 64 + L) * 16 + (c & 15)]
-                        out[row, c0 + c] = (s << 15) | (e << 8) | int(m)
+    seen = np.zeros((n, k), dtype=bool)
+    for item in range(h["n_items"]):
+        for L in range(64):
+            row, c0 = lane_place(h, item, L)
+            bits = lane_bits(blob, h, item, L)
+            assert bits[0] == 0 and bits[1] == 0
+            real = max(0, min(k - c0, C)) if row < n else 0
+            pos = 2
+            padded = list(bits) + [0] * 32
+            for c in range(real):
+                if fp8:
+                    b, pos = _parse_fp8(padded, pos, r2s)
+                    out[row, c0 + c] = b
+                else:
+                    s, e, pos = O.parse_one_bf16(padded, pos, r2s)
+                    out[row, c0 + c] = (s << 15) | (e << 8) | int(mant_byte(blob, h, item, L, c))
+                seen[row, c0 + c] = True
+            assert not np.any(bits[pos:]), (item, L)
+            if not fp8:
+                for c in range(real, C):
+                    assert mant_byte(blob, h, item, L, c) == 0, (item, L, c)
+    assert seen.all()
     return out
 
 

@@ -46,7 +46,7 @@ def test_encoder_matches_oracle_rank_and_size(name, w):
     enc = O.encode_bf16(w)
     assert info["rank_to_sym"] == [int(v) for v in enc["rank_to_sym"]]
     assert info["coded_bits"] == enc["coded_bits"]
-    assert info["n"], info["k"] == w.shape
+    assert (info["n"], info["k"]) == w.shape
 
 
 def test_encoder_fp8_matches_oracle():
@@ -59,15 +59,38 @@ def test_encoder_fp8_matches_oracle():
         assert info["coded_bits"] == enc["coded_bits"]
 
 
-@pytest.mark.parametrize("shape,cols,seed", [((70, 333), 64, 1), ((130, 100), 0, 2), ((3, 600), 256, 3),
-                                             ((64, 48), 16, 4)])
-def test_blob_layout_decodes_to_input(shape, cols, seed):
+# (shape, cols_per_lane, rows_per_wave): automatic, every lane count per row
+# (R = 64 .. 1), ragged K and N, and a row split over two workgroups.
+@pytest.mark.parametrize("shape,cols,rows,seed", [((70, 333), 16, 8, 1), ((130, 100), 0, 0, 2), ((3, 600), 64, 1, 3),
+                                                  ((64, 48), 16, 64, 4), ((9, 1000), 48, 2, 5), ((33, 257), 32, 32, 6),
+                                                  ((2, 66000), 64, 1, 7)])
+def test_blob_layout_decodes_to_input(shape, cols, rows, seed):
     w = S.inject_rare(S.student_t_bf16(seed, shape), seed + 7, frac=0.02)
-    blob = nwc.encode(w, cols_per_item=cols)
+    blob = nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows)
+    info = nwc.blob_info(blob)
+    if cols:
+        assert (info["cols_per_lane"], info["rows_per_wave"]) == (cols, rows)
     assert np.array_equal(BL.decode_blob(blob), w)
     q, _ = S.fp8_quantize(w)
-    blob8 = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_item=cols)
+    blob8 = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_lane=cols, rows_per_wave=rows)
     assert np.array_equal(BL.decode_blob(blob8), q)
+
+
+def test_two_span_geometry():
+    blob = nwc.encode(S.normal_bf16(8, (2, 66000), 0.02), cols_per_lane=64, rows_per_wave=1)
+    info = nwc.blob_info(blob)
+    # 1032 slices of 64 columns, 64 per wave: 17 waves, more than a workgroup holds.
+    assert (info["n_spans"], info["waves_per_group"]) == (2, 9)
+    assert info["n_items"] == 2 * 2 * 9
+
+
+def test_auto_geometry_of_the_layer_shapes():
+    # Every Qwen3-4B projection fits one workgroup per row group (no span sums).
+    for (n, k), want in [((1024, 2560), (16, 4, 10)), ((4096, 2560), (32, 8, 10)), ((2560, 4096), (32, 8, 16)),
+                         ((2560, 9728), (48, 4, 13))]:
+        info = nwc.blob_info(nwc.encode(S.normal_bf16(1, (n, k), 0.02)))
+        assert (info["cols_per_lane"], info["rows_per_wave"], info["waves_per_group"]) == want, (n, k)
+        assert info["n_spans"] == 1
 
 
 def test_all_patterns_blob_layout():
@@ -127,13 +150,17 @@ def test_encoder_argument_errors():
     blob = np.zeros(1 << 20, np.uint8)
     size = ctypes.c_int64()
     L = nwc.lib
-    assert L.nwc_encode(None, 4, 8, 8, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -1
-    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 7, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -1
-    assert L.nwc_encode(w.ctypes.data, 4, 8, 4, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -2
-    assert L.nwc_encode(w.ctypes.data, 0, 8, 8, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -2
-    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 24, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == -1
-    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 0, blob.ctypes.data, 100, ctypes.byref(size)) == -3
-    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 0, blob.ctypes.data, blob.nbytes, ctypes.byref(size)) == 0
+    enc = lambda *a: L.nwc_encode(*a, blob.ctypes.data, blob.nbytes, ctypes.byref(size))
+    assert enc(None, 4, 8, 8, 0, 0, 0) == -1
+    assert enc(w.ctypes.data, 4, 8, 8, 7, 0, 0) == -1      # element type
+    assert enc(w.ctypes.data, 4, 8, 4, 0, 0, 0) == -2      # ld < k
+    assert enc(w.ctypes.data, 0, 8, 8, 0, 0, 0) == -2
+    assert enc(w.ctypes.data, 4, 8, 8, 0, 24, 0) == -1     # cols_per_lane not a multiple of 16
+    assert enc(w.ctypes.data, 4, 8, 8, 0, 128, 0) == -1    # cols_per_lane too large
+    assert enc(w.ctypes.data, 4, 8, 8, 0, 0, 6) == -1      # rows_per_wave not a power of two
+    assert enc(w.ctypes.data, 4, 8, 8, 0, 0, 128) == -1
+    assert L.nwc_encode(w.ctypes.data, 4, 8, 8, 0, 0, 0, blob.ctypes.data, 100, ctypes.byref(size)) == -3
+    assert enc(w.ctypes.data, 4, 8, 8, 0, 0, 0) == 0
     with pytest.raises(TypeError):
         nwc.encode(w.astype(np.float32))
 
@@ -142,20 +169,23 @@ def test_bound_covers_worst_case():
     # The all-escape matrix (every symbol ties) is the longest code there is.
     w = S.all_patterns_bf16()
     assert nwc.encode(w).nbytes <= nwc.encode_bound(256, 256)
-    for cols in (16, 64, 256):
-        assert nwc.encode(w, cols_per_item=cols).nbytes <= nwc.encode_bound(256, 256, 0, cols)
+    for cols in (16, 32, 64):
+        for rows in (1, 8, 64):
+            assert nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows).nbytes <= \
+                nwc.encode_bound(256, 256, 0, cols, rows)
+
+
+def _two_span():
+    w = S.normal_bf16(3, (200, 66000), 0.02)
+    return w, nwc.encode(w, cols_per_lane=64, rows_per_wave=1)
 
 
 def test_header_validation_and_workspace():
-    w = S.normal_bf16(3, (200, 700), 0.02)
-    blob = nwc.encode(w, cols_per_item=128)
+    w, blob = _two_span()
     hdr = blob[:256].copy()
-    ws = nwc.workspace_size(hdr)
     info = nwc.blob_info(blob)
-    n_rb = (200 + 63) // 64
-    n_ks_pad = (((700 + 127) // 128) + 3) // 4 * 4
-    assert ws == ((n_rb * 64 * n_ks_pad * 4 + 255) // 256) * 256
-    assert info["n_items"] == n_rb * ((700 + 127) // 128)
+    assert info["n_spans"] == 2
+    assert nwc.workspace_size(hdr) == ((200 * 4 * 4 + 255) // 256) * 256   # [row][span padded to 4] fp32
     bad = hdr.copy()
     bad[0] ^= 1
     with pytest.raises(nwc.NWCError) as ei:
@@ -165,13 +195,16 @@ def test_header_validation_and_workspace():
     bad[8] = 5  # elem
     with pytest.raises(nwc.NWCError):
         nwc.blob_info(np.concatenate([bad, blob[256:]]))
-    # A single column span needs no workspace.
-    assert nwc.workspace_size(nwc.encode(S.normal_bf16(3, (70, 100), 0.02), cols_per_item=128)[:256].copy()) == 0
+    bad = hdr.copy()
+    bad[36] = 3  # rows_per_wave not a power of two
+    with pytest.raises(nwc.NWCError):
+        nwc.workspace_size(bad)
+    # A row held by one workgroup needs no workspace.
+    assert nwc.workspace_size(nwc.encode(S.normal_bf16(3, (70, 100), 0.02))[:256].copy()) == 0
 
 
 def test_launchers_reject_bad_arguments_before_any_gpu_call():
-    w = S.normal_bf16(3, (200, 700), 0.02)
-    blob = nwc.encode(w, cols_per_item=128)
+    w, blob = _two_span()
     hdr = blob[:256].copy()
     L = nwc.lib
     fake = 1 << 20  # never dereferenced: every call below fails its host-side checks
@@ -185,11 +218,11 @@ def test_launchers_reject_bad_arguments_before_any_gpu_call():
     bad = hdr.copy()
     bad[4] = 9  # version
     assert L.nwc_matvec(bad.ctypes.data, fake, fake, None, fake, fake, ws, None) == -4
-    assert L.nwc_dequant(hdr.ctypes.data, fake, fake, 699, None) == -2
-    assert L.nwc_dequant(hdr.ctypes.data, fake, fake + 2, 700, None) == -1
+    assert L.nwc_dequant(hdr.ctypes.data, fake, fake, 65999, None) == -2
+    assert L.nwc_dequant(hdr.ctypes.data, fake, fake + 2, 66000, None) == -1
     assert L.nwc_gather(hdr.ctypes.data, fake, fake, -1, fake, None) == -2
     assert L.nwc_gather(hdr.ctypes.data, fake, fake + 4, 5, fake, None) == -1
     assert L.nwc_gather(hdr.ctypes.data, fake, fake, 0, fake, None) == 0   # nothing to do
-    q, _ = S.fp8_quantize(w)
-    h8 = nwc.encode(q, elem=1, cols_per_item=128)[:256].copy()
-    assert L.nwc_matvec(h8.ctypes.data, fake, fake, None, fake, fake, ws, None) == -1   # fp8 needs a scale
+    q, _ = S.fp8_quantize(S.normal_bf16(3, (200, 700), 0.02))
+    h8 = nwc.encode(q, elem=1)[:256].copy()
+    assert L.nwc_matvec(h8.ctypes.data, fake, fake, None, fake, None, 0, None) == -1   # fp8 needs a scale

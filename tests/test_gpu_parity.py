@@ -57,9 +57,9 @@ def dequant_host(dm, ld=None):
     return (o.view(np.uint16) if dm.elem == 0 else o)[:, :dm.k]
 
 
-def full_parity_bf16(w, x, cols=0, check_matvec=True):
-    print(f"case shape={w.shape} cols={cols}", flush=True)
-    dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_item=cols), DEV)
+def full_parity_bf16(w, x, cols=0, rows=0, check_matvec=True):
+    print(f"case shape={w.shape} cols={cols} rows={rows}", flush=True)
+    dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows), DEV)
     enc = O.encode_bf16(w)
     assert np.array_equal(dequant_host(dm), O.decode_bf16(enc))
     if check_matvec:
@@ -72,11 +72,38 @@ def full_parity_bf16(w, x, cols=0, check_matvec=True):
 
 
 # ----------------------------------------------------------------- single 1024 x 1024
-@pytest.mark.parametrize("cols", [0, 16, 64, 128, 256])
-def test_single_matrix(cols):
+# Work-item geometries (cols_per_lane, rows_per_wave): automatic; one lane per
+# row with the row over 4 workgroups (span sums); 64 lanes per row in one
+# wave; and the widths 32/48/64 with 8, 16 or 32 lanes per row.
+GEOMETRIES = [(0, 0), (16, 64), (16, 1), (32, 8), (48, 4), (64, 2), (64, 16)]
+
+
+@pytest.mark.parametrize("cols,rows", GEOMETRIES)
+def test_single_matrix(cols, rows):
     w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
     x = S.activation_bf16(C.SINGLE["x_seed"], 1024)
-    full_parity_bf16(w, x, cols)
+    full_parity_bf16(w, x, cols, rows)
+
+
+def test_row_over_two_workgroups():
+    w = S.normal_bf16(41, (200, 66000), 0.02)
+    x = S.activation_bf16(42, 66000)
+    dm = full_parity_bf16(w, x, 64, 1)
+    assert dm.info["n_spans"] == 2
+
+
+def test_fillers_when_rank0_is_the_top_symbol():
+    # Most weights have exponent symbol 0x7F, so rank 0 is 0x7F and a filler
+    # (zero code bits, zero mantissa) decodes to 0x7F00 = 2^127: finite, and
+    # times the zero activation past column K it must add exactly zero.
+    rng = np.random.default_rng(43)
+    n, k = 7, 513
+    w = (0x7F00 | rng.integers(0, 0x80, size=(n, k)) | (rng.integers(0, 2, size=(n, k)) << 15)).astype(np.uint16)
+    w[0, :5] = S.normal_bf16(44, (1, 5), 0.02)[0]
+    x = S.bf16_from_f32((rng.standard_normal(k) * 1e-30).astype(np.float32))
+    for cols, rows in ((0, 0), (32, 8), (64, 1)):
+        dm = full_parity_bf16(w, x, cols, rows)
+        assert dm.info["rank_to_sym"][0] == 0x7F
 
 
 def test_dequant_row_pitch():
@@ -139,8 +166,8 @@ def test_fp8_single_matrix():
     w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
     x = S.activation_bf16(C.SINGLE["x_seed"], 1024)
     q, sc = S.fp8_quantize(w)
-    for cols in (0, 128, 256):
-        dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_item=cols), DEV)
+    for cols, rows in ((0, 0), (16, 64), (32, 8), (64, 1)):
+        dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_lane=cols, rows_per_wave=rows), DEV)
         assert np.array_equal(dequant_host(dm), O.decode_fp8(O.encode_fp8(q)))
         y_ref, A = O.matvec_fp8_ref(q, sc, x)
         check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8")

@@ -91,28 +91,34 @@ def time_region(torch, fn, steps, warmup):
 
 
 def cpu_baseline(S, C):
-    """The oracle (decode + float64 matvec) on one q matrix of the layer set, on host cores."""
+    """The oracle (decode + float64 matvec) on host cores, on a bounded sample of
+    the layer set: layer 0's q, k, v, o and gate matrices (51 M weights)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
-    name, n, k = C.QWEN3_4B[1]  # k projection, 1024 x 2560
-    ws, xs = C.qwen3_seed(0, 1)
-    w = S.normal_bf16(ws, (n, k), C.sigma_for(k))  # host generator: same shape and distribution
-    x = S.activation_bf16(xs, k)
-    enc = O.encode_bf16(w)
-    ctx = threadpool_limits(1) if threadpool_limits else None
+    sample = [s for s in C.QWEN3_4B if s[0] in ("q", "k", "v", "o", "gate")]
+    work, gbytes, weights = [], 0.0, 0
+    for name, n, k in sample:
+        idx = [s[0] for s in C.QWEN3_4B].index(name)
+        ws, xs = C.qwen3_seed(0, idx)
+        w = S.normal_bf16(ws, (n, k), C.sigma_for(k))  # host generator: same shapes and distribution
+        enc = O.encode_bf16(w)
+        del w
+        work.append((enc, S.activation_bf16(xs, k)))
+        gbytes += (enc["coded_bits"] / 8.0 + 2 * k + 4 * n) / 1e9
+        weights += n * k
+    limit = threadpool_limits(1) if threadpool_limits else None
     t0 = time.perf_counter()
-    wd = O.decode_bf16(enc)
-    y, A = O.matvec_bf16_ref(wd, x)
+    for enc, x in work:
+        y, A = O.matvec_bf16_ref(O.decode_bf16(enc), x)
     dt = time.perf_counter() - t0
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
-    gb = (enc["coded_bits"] / 8.0 + 2 * k + 4 * n) / 1e9
-    return {"value": round(gb / dt, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle decode + float64 matvec of one {n}x{k} matrix of the layer set "
-                      f"(host PCG64 draws of the same distribution), single thread, {dt:.2f} s"}
+    if limit is not None and hasattr(limit, "unregister"):
+        limit.unregister()
+    return {"value": round(gbytes / dt, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle decode + float64 matvec of layer 0's q, k, v, o, gate ({weights / 1e6:.1f} M weights, "
+                      f"host PCG64 draws of the same distributions), single thread, {dt:.1f} s"}
 
 
 def main():
@@ -123,6 +129,11 @@ def main():
     ap.add_argument("--layers", type=int, default=36)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--profile-sweeps", type=int, default=0,
+                    help="run this many eager sweeps and exit, untimed (for rocprofv3 counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the sweeps, copy 256 MiB device->device once, a reference dispatch of known "
+                         "size for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -136,12 +147,31 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    mats = build_layer_set(torch, nwc, S, C, dev, args.layers, not args.no_bf16_baseline)
+    mats = build_layer_set(torch, nwc, S, C, dev, args.layers,
+                           not args.no_bf16_baseline and not args.profile_sweeps)
     n_launch = len(mats)
 
     def sweep():
         for m in mats:
             m["dm"].matvec(m["x"], m["y"])
+
+    if args.profile_sweeps:
+        if args.copy_calibration:
+            src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        for _ in range(args.profile_sweeps):
+            sweep()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_sweeps": args.profile_sweeps, "matvecs_per_sweep": n_launch,
+                          "algo_bytes_per_matvec": sum(m["algo_bytes"] for m in mats) / n_launch,
+                          "blob_bytes_per_matvec": sum(m["blob_bytes"] for m in mats) / n_launch,
+                          "copy_calibration_bytes": (64 << 20) * 4 if args.copy_calibration else 0,
+                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+        return
 
     # The sweep is captured once as a HIP graph and replayed: 252 launches per
     # step from Python would otherwise be limited by host launch overhead,

@@ -7,6 +7,8 @@
 // layout (work items of R rows x 64/R column slices, one lane per slice) is
 // described in nwc_format.h.
 #include <algorithm>
+#include <climits>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <thread>
@@ -154,33 +156,53 @@ Geo make_geo(int64_t n, int64_t k, int C, int R, int max_waves) {
   return g;
 }
 
+// Code rows a lane of C columns is likely to need, from the histogram: the
+// mean stream length plus six standard deviations (fillers are short, so a
+// full lane of real weights is the long case).  Only used to rule out
+// geometries whose workgroup would not fit the decoder's LDS; the exact
+// rows are planned afterwards.
+struct RowEstimate {
+  double mean = 0, var = 0;  // code bits per weight
+  uint32_t rows(int C) const {
+    const double bits = NWC_LEAD_BITS + C * mean + 6.0 * std::sqrt(C * var);
+    return (uint32_t)std::ceil(bits / 32.0);
+  }
+};
+
 // Automatic geometry.  Lanes decode C/2 (BF16) code pairs one after the
-// other, so C bounds a wave's decode latency; small matrices get C = 16 to
-// have enough waves.  Among the row counts R whose row group fits one
-// workgroup, pick the one that stores the fewest filler columns, then the
-// largest R (fewer, larger workgroups per decode table copy).  If that still
-// pads more than 3%, a wider C may pad less.
-Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req) {
+// other, so C bounds a wave's decode latency: C = 32, or 16 for matrices too
+// small to give thousands of waves otherwise (wider C only when no 32-column
+// geometry fits).  Among the row counts R whose row group fits one workgroup
+// within the LDS budget, the cost is the stored lane columns (fillers count)
+// times a penalty for workgroups far from 5 waves -- measured on MI355X
+// across the Qwen-shaped matrices: 4-5 waves per workgroup were fastest,
+// 8-10 took 5-20% longer, 2-3 (with padding) longer still.
+double wave_penalty(int W) { return 1.0 + 0.04 * std::max(0, W - 5) + 0.05 * std::max(0, 4 - W); }
+
+Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req, const RowEstimate &est) {
   std::vector<int> Cs, Rs;
   if (C_req) Cs = {C_req};
-  else Cs = {n * k < ((int64_t)1 << 23) ? 16 : 32, 48, 64};
+  else if (n * k < ((int64_t)1 << 23)) Cs = {16, 32, 48, 64};
+  else Cs = {32, 48, 64};
   if (R_req) Rs = {R_req};
   else Rs = {64, 32, 16, 8, 4, 2, 1};
-  Geo best;
-  int64_t best_cols = INT64_MAX;
   for (int C : Cs) {
+    Geo best;
+    double best_cost = 0;
     for (int R : Rs) {
       const Geo g = make_geo(n, k, C, R, NWC_MAX_WAVES);
-      if (g.n_spans != 1 && !(R_req && C_req)) continue;
-      if (g.lane_cols() < best_cols) {
+      if (C_req && R_req) return g;
+      if (g.n_spans != 1) continue;
+      if (nwc_lds_bytes_for(g.W, g.R, est.rows(C)) > NWC_LDS_BUDGET) continue;
+      const double cost = (double)g.lane_cols() * wave_penalty(g.W);
+      if (!best.C || cost < best_cost) {
         best = g;
-        best_cols = g.lane_cols();
+        best_cost = cost;
       }
     }
-    if (best.C && (double)best_cols <= 1.03 * (double)n * (double)k) break;
+    if (best.C) return best;
   }
-  if (!best.C) best = make_geo(n, k, Cs.back(), R_req ? R_req : 1, NWC_MAX_WAVES);  // k > 65536: several spans
-  return best;
+  return make_geo(n, k, Cs.back(), R_req ? R_req : 1, NWC_MAX_WAVES);  // k > 65536: several spans
 }
 
 // Lane L of item `item`: matrix row and first column (may lie past n / k).
@@ -224,11 +246,7 @@ std::vector<uint32_t> plan_rows(const void *w, int64_t n, int64_t k, int64_t ld,
   return rows;
 }
 
-// Decoder LDS for one workgroup: staged code rows of W waves (+ guard rows),
-// the cross-wave row sums, the static decode table.
-int64_t lds_need(const Geo &g, uint32_t max_rows) {
-  return (int64_t)g.W * (max_rows + NWC_GUARD_ROWS) * 256 + (int64_t)g.W * g.R * 4 + NWC_LUT_BYTES;
-}
+int64_t lds_need(const Geo &g, uint32_t max_rows) { return nwc_lds_bytes_for(g.W, g.R, max_rows); }
 
 int64_t bound_bytes(int64_t n, int64_t k, int elem, int C_req, int R_req) {
   // Worst case over every admissible geometry: 16 code bits per weight.
@@ -327,7 +345,19 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
 
   // 3. work-item geometry; fewer waves per workgroup (more column spans) if
   // the staged code rows of a workgroup would not fit the decoder's LDS.
-  Geo g = auto_geo(n, k, cols_per_lane, rows_per_wave);
+  RowEstimate est;
+  {
+    double total = 0, s1 = 0, s2 = 0;
+    for (int sy = 0; sy < alphabet; ++sy) {
+      const double l = tab.len[elem == NWC_BF16 ? sy : (sy << 3)];
+      total += (double)counts[sy];
+      s1 += (double)counts[sy] * l;
+      s2 += (double)counts[sy] * l * l;
+    }
+    est.mean = s1 / total;
+    est.var = std::max(0.0, s2 / total - est.mean * est.mean);
+  }
+  Geo g = auto_geo(n, k, cols_per_lane, rows_per_wave, est);
   std::vector<uint32_t> rows;
   for (int mw = NWC_MAX_WAVES;; --mw) {
     rows = plan_rows(w, n, k, ld, elem, tab, g);

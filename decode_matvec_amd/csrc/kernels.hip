@@ -32,6 +32,11 @@
 //    to finite values, so padding adds exactly zero.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "nwc_check.h"
 
 namespace {
@@ -186,33 +191,35 @@ __device__ __forceinline__ uint32_t bf16_step(Lane &s) {
 // ----------------------------------------------------------------- staging
 typedef __attribute__((address_space(3))) void lds_void;
 
-// 1 KiB global -> LDS straight into LDS (no registers), lane L moving bytes
-// [16L, 16L+16); lanes past `bytes` do nothing.
-__device__ __forceinline__ void dma_1k(const uint8_t *src, uint32_t *dst, uint32_t bytes, uint32_t lane) {
+// 1 KiB global -> LDS (byte address dst) straight into LDS (no registers),
+// lane L moving bytes [16L, 16L+16); lanes past `bytes` do nothing.
+__device__ __forceinline__ void dma_1k(const uint8_t *src, uint32_t dst, uint32_t bytes, uint32_t lane) {
   if (lane * 16 < bytes)
-    __builtin_amdgcn_global_load_lds(src + lane * 16, (lds_void *)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + lane * 16, (lds_void *)(size_t)dst, 16, 0, 0);
 }
 
 // This wave's share of a copy global -> LDS, 1 KiB per instruction.
-__device__ __forceinline__ void dma_to_lds(const uint8_t *src, uint32_t *dst, uint32_t bytes, uint32_t lane) {
-  for (uint32_t off = 0; off < bytes; off += 1024) dma_1k(src + off, dst + off / 4, bytes - off, lane);
+__device__ __forceinline__ void dma_to_lds(const uint8_t *src, uint32_t dst, uint32_t bytes, uint32_t lane) {
+  for (uint32_t off = 0; off < bytes; off += 1024) dma_1k(src + off, dst + off, bytes - off, lane);
 }
 
-// The decode table in 16 pieces of 1 KiB; wave w of W copies pieces w, w+W, ...
-__device__ __forceinline__ void dma_lut(const Geom &g, uint32_t *lut, uint32_t wave, uint32_t lane) {
-  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += g.W)
-    dma_1k(g.blob + g.off_lut + p * 1024, lut + p * 256, 1024, lane);
+// The decode table in 16 pieces of 1 KiB; wave w of `waves` copies pieces w, w+waves, ...
+__device__ __forceinline__ void dma_lut(const Geom &g, uint32_t lut, uint32_t wave, uint32_t waves, uint32_t lane) {
+  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += waves)
+    dma_1k(g.blob + g.off_lut + p * 1024, lut + p * 1024, 1024, lane);
 }
 
-// Copies item `item`'s code rows into the wave's LDS region and zeroes the
-// two guard rows after them (this lane's column only; the lane is the only
-// reader of its column).
+__device__ __forceinline__ void lds_store(uint32_t byte_addr, uint32_t v) { *(lds_u32 *)(size_t)byte_addr = v; }
+
+// Copies item `item`'s code rows into the wave's LDS region (byte address
+// `region`) and zeroes the two guard rows after them (this lane's column
+// only; the lane is the only reader of its column).
 __device__ __forceinline__ void stage_code(const Geom &g, const uint32_t *__restrict__ items, uint32_t item,
-                                           uint32_t *region, uint32_t lane) {
+                                           uint32_t region, uint32_t lane) {
   const uint32_t off = items[2 * item], rows = items[2 * item + 1];
   dma_to_lds(g.blob + g.off_code + off, region, rows * 256, lane);
-  region[rows * 64 + lane] = 0u;
-  region[(rows + 1) * 64 + lane] = 0u;
+  lds_store(region + rows * 256 + 4 * lane, 0u);
+  lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
 }
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -326,48 +333,132 @@ __device__ __forceinline__ void store_row(const Geom &g, int64_t row, uint32_t s
     partial[(uint64_t)row * spans_pad(g.n_spans) + span] = v;
 }
 
-// Workgroup = one row group (x one column span).  Every wave stages its code
-// rows, mantissas and activations, then decodes its C columns per lane; the
-// row sums close over the row's lanes and the workgroup's waves.
-template <bool FP8, int NG>
+// Sum of the S adjacent lanes of each row (S a power of two, 1..64), left in
+// the row's last lane (lane r*S + S-1); other lanes hold partial windows.
+// DPP adds in a fixed order: row_shr 1, 2, 4, 8 sum windows of up to 16
+// lanes inside each 16-lane row, row_bcast:15 / row_bcast:31 join rows.
+__device__ __forceinline__ float row_sum_lanes(float a, uint32_t S) {
+  if (S >= 2) a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x111, 0xF, 0xF, true));
+  if (S >= 4) a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x112, 0xF, 0xF, true));
+  if (S >= 8) a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x114, 0xF, 0xF, true));
+  if (S >= 16) a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x118, 0xF, 0xF, true));
+  if (S >= 32) a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x142, 0xA, 0xF, false));
+  if (S >= 64) a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x143, 0xC, 0xF, false));
+  return a;
+}
+
+// Waits until at most one vector memory operation of this wave is still in
+// flight (`one`: the row-sum store just issued) or none.
+__device__ __forceinline__ void wait_loads_keep_store(bool one) {
+  if (one)
+    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Persistent workgroups: workgroup b decodes the row groups (x column spans)
+// [b*G/grid, (b+1)*G/grid) of the G = n_rowgroups * n_spans in order.  The
+// decode table (and, with one span per row, the activations) is staged once
+// per workgroup.  With PF, each group's code rows and mantissas are requested
+// while the previous group decodes (two LDS code regions per wave, two
+// mantissa register sets); without it a group's loads follow the previous
+// group's row sums.
+template <bool FP8, int NG, bool PF>
 __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__restrict__ items,
                                                       const uint16_t *__restrict__ x,
                                                       const float *__restrict__ scale, float *__restrict__ y,
                                                       float *__restrict__ partial) {
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
-  extern __shared__ uint32_t s_dyn[];  // W code regions, then W*R row sums
+  extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Place pl = place(g, blockIdx.x, wave, lane);
-  uint32_t *region = s_dyn + wave * g.region_words;
+  const uint32_t n_groups = g.n_rowgroups * g.n_spans;
+  const uint32_t first = (uint32_t)((uint64_t)blockIdx.x * n_groups / gridDim.x);
+  const uint32_t last = (uint32_t)((uint64_t)(blockIdx.x + 1) * n_groups / gridDim.x);
+  // Dynamic LDS: (PF ? 2 : 1) code regions per wave, then two sets of W*R
+  // row sums (matvec_lds on the host sizes it the same way).
+  const uint32_t region0 = lds_addr(s_dyn) + (PF ? 2 : 1) * wave * g.region_words * 4;  // LDS byte addresses
+  const uint32_t region_bytes = g.region_words * 4;
+  float *red = (float *)(s_dyn + (PF ? 2 : 1) * g.W * g.region_words);  // after the code regions
 
-  dma_lut(g, s_lut, wave, lane);
-  stage_code(g, items, pl.item, region, lane);
-  uint4 m[NG];
-  if (!FP8) {
-    const uint4 *mp = mant_base(g, pl.item, lane);
-#pragma unroll
-    for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
-  }
+  dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
+  Place pl = place(g, first, wave, lane);
   X16 xv[NG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, pl.c0 + 16 * j, g.k);
+  uint4 mn[NG];
+  stage_code(g, items, pl.item, region0, lane);
+  if (!FP8) {
+    const uint4 *mp = mant_base(g, pl.item, lane);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
+  }
   staged_barrier();
 
-  Lane st{lds_addr(region) + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
-  float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
-  for (uint32_t d = 1; d < g.S; d <<= 1) a += __shfl_xor(a, (int)d);  // same bits in all S lanes
-  if (g.W == 1) {
-    if (pl.s == 0) store_row(g, pl.row, pl.span, a, scale, y, partial, FP8);
-    return;
-  }
-  float *red = (float *)(s_dyn + g.W * g.region_words);
-  if (pl.s == 0) red[wave * g.R + pl.r] = a;
-  __syncthreads();
-  if (wave == 0 && lane < g.R) {
-    float t = 0.f;
-    for (uint32_t w = 0; w < g.W; ++w) t += red[w * g.R + lane];
-    store_row(g, (int64_t)pl.row_group * g.R + lane, pl.span, t, scale, y, partial, FP8);
+  bool stored = false;
+  uint32_t buf = 0;
+  for (uint32_t grp = first; grp < last; ++grp, buf ^= (PF ? 1u : 0u)) {
+    const Place cur = place(g, grp, wave, lane);
+    if (!PF && grp != first) {
+      // Single buffer: this group's loads start now, after the last group's sums.
+      if (g.n_spans > 1) {
+#pragma unroll
+        for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
+      }
+      stage_code(g, items, cur.item, region0, lane);
+      if (!FP8) {
+        const uint4 *mp = mant_base(g, cur.item, lane);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
+      }
+      wait_all_loads();
+    }
+    // This group's data arrived; take its mantissas before the next group's
+    // loads reuse mn.
+    uint4 m[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) m[j] = mn[j];
+    if (PF && g.n_spans > 1 && grp != first) {
+#pragma unroll
+      for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
+    }
+    if (PF && grp + 1 < last) {
+      const Place nxt = place(g, grp + 1, wave, lane);
+      stage_code(g, items, nxt.item, region0 + (buf ^ 1u) * region_bytes, lane);
+      if (!FP8) {
+        const uint4 *mp = mant_base(g, nxt.item, lane);
+#pragma unroll
+        for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
+      }
+    }
+    Lane st{region0 + buf * region_bytes + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
+    float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
+    a = row_sum_lanes(a, g.S);
+    const bool row_lane = pl.s == g.S - 1u;
+    stored = false;
+    if (g.W == 1) {
+      if (row_lane) store_row(g, cur.row, cur.span, a, scale, y, partial, FP8);
+      stored = true;
+    } else {
+      // Row sums alternate between two buffers by group parity: wave 0 may
+      // still read this group's while a faster wave writes the next group's.
+      float *rb = red + ((grp - first) & 1u) * g.W * g.R;
+      if (row_lane) rb[wave * g.R + pl.r] = a;
+      // LDS writes done, then a bare barrier: __syncthreads() would also wait
+      // for the next group's loads, issued above to overlap this decode.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (wave == 0) {
+        if (lane < g.R) {
+          float t = 0.f;
+          for (uint32_t w = 0; w < g.W; ++w) t += rb[w * g.R + lane];
+          store_row(g, (int64_t)cur.row_group * g.R + lane, cur.span, t, scale, y, partial, FP8);
+        }
+        stored = true;
+      }
+    }
+    if (PF && grp + 1 < last) wait_loads_keep_store(stored);
   }
 }
 
@@ -456,11 +547,11 @@ __global__ __launch_bounds__(1024) void dequant_kernel(Geom g, const uint32_t *_
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Place pl = place(g, blockIdx.x, wave, lane);
-  uint32_t *region = s_dyn + wave * g.region_words;
-  dma_lut(g, s_lut, wave, lane);
+  const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
+  dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
   stage_code(g, items, pl.item, region, lane);
   staged_barrier();
-  Lane st{lds_addr(region) + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
+  Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
   const int64_t esz = FP8 ? 1 : 2;
   const bool real = pl.row < g.n;
   const bool vec = (ld * esz) % 16 == 0;
@@ -482,9 +573,8 @@ __global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t waves = blockDim.x >> 6;
-  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += waves)
-    dma_1k(g.blob + g.off_lut + p * 1024, s_lut + p * 256, 1024, lane);
-  uint32_t *region = s_dyn + wave * g.region_words;
+  dma_lut(g, lds_addr(s_lut), wave, waves, lane);
+  const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tok = t / n_sl;
   const uint32_t q = (uint32_t)(t - tok * n_sl);
@@ -498,16 +588,16 @@ __global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__
   const uint32_t item = (rg * g.n_spans + span) * g.W + wv, L = r * g.S + s;
   const uint32_t off = items[2 * item], rows = items[2 * item + 1];
   const uint32_t *src = (const uint32_t *)(g.blob + g.off_code + off) + L;
-  for (uint32_t i = 0; i < rows; ++i) region[i * 64 + lane] = src[i * 64];
-  region[rows * 64 + lane] = 0u;
-  region[(rows + 1) * 64 + lane] = 0u;
+  for (uint32_t i = 0; i < rows; ++i) lds_store(region + i * 256 + 4 * lane, src[i * 64]);
+  lds_store(region + rows * 256 + 4 * lane, 0u);
+  lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
   staged_barrier();
   const int64_t esz = FP8 ? 1 : 2;
   const int64_t c0 = (int64_t)q * g.C;
   uint8_t *dst = out + (tok * g.k + c0) * esz;
   const bool vec = (g.k * esz) % 16 == 0;
   if (valid) {
-    Lane st{lds_addr(region) + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
+    Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
     slice_decode<FP8, NG>(st, FP8 ? nullptr : mant_base(g, item, L), [&](int gi, const uint32_t(&v)[8]) {
       put_group<FP8>(dst + 16 * gi * esz, v, g.k - c0 - 16 * gi, vec);
     });
@@ -540,8 +630,11 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
   return g;
 }
 
-// Dynamic LDS of a matvec / dequant workgroup: W code regions + W*R row sums.
+// Dynamic LDS of a dequant workgroup: W code regions + W*R row sums; of a
+// matvec workgroup: one or two (double buffered) code regions per wave and
+// two sets of row sums.
 size_t group_lds(const Geom &g) { return (size_t)g.W * g.region_words * 4 + (size_t)g.W * g.R * 4; }
+size_t matvec_lds(const Geom &g, bool pf) { return (pf ? 2 : 1) * (size_t)g.W * g.region_words * 4 + 2 * (size_t)g.W * g.R * 4; }
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -555,11 +648,64 @@ int read_header(const void *header, nwc_header_t &h) {
 
 const uint32_t *item_table(const Geom &g) { return (const uint32_t *)(g.blob + g.off_items); }
 
+// Workgroups a launch keeps resident at once on this device (occupancy
+// query, cached per kernel, block size and LDS), times the compute units.
+int resident_groups(const void *kernel, int block, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void *, int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, kernel, block, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cache[key] = per_cu * cus;
+}
+
+// Persistent grid: as many workgroups as fit at once, each taking the same
+// number of groups (so no workgroup runs a round more than the others).
+// NWC_PERSIST=0 gives one workgroup per group (for comparisons).
+uint32_t matvec_grid(const Geom &g, const void *kernel, size_t lds) {
+  const uint32_t n_groups = g.n_rowgroups * g.n_spans;
+  static const bool off = [] {
+    const char *e = getenv("NWC_PERSIST");
+    return e && e[0] == '0';
+  }();
+  const int cap = off ? 0 : resident_groups(kernel, g.W * 64, lds);
+  if (cap <= 0 || (uint32_t)cap >= n_groups) return n_groups;
+  const uint32_t rounds = (n_groups + cap - 1) / cap;
+  return (n_groups + rounds - 1) / rounds;
+}
+
+// Double-buffered group loads: measured slower than single-buffered
+// persistent workgroups on every Qwen-shaped matrix (the second code region
+// halves how many workgroups fit a CU), so off unless NWC_PF=1.
+bool prefetch_groups() {
+  static const bool on = [] {
+    const char *e = getenv("NWC_PF");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+template <bool FP8, int NG, bool PF>
+void launch_matvec_pf(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
+  const void *kernel = (const void *)matvec_kernel<FP8, NG, PF>;
+  const size_t lds = matvec_lds(g, PF);
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG, PF>), dim3(matvec_grid(g, kernel, lds)), dim3(g.W * 64), lds, s, g,
+                     item_table(g), (const uint16_t *)d_x, d_scale, d_y, partial);
+}
+
 template <bool FP8, int NG>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
-  const dim3 grid(g.n_rowgroups * g.n_spans), block(g.W * 64);
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG>), grid, block, group_lds(g), s, g, item_table(g),
-                     (const uint16_t *)d_x, d_scale, d_y, partial);
+  if (prefetch_groups())
+    launch_matvec_pf<FP8, NG, true>(g, s, d_x, d_scale, d_y, partial);
+  else
+    launch_matvec_pf<FP8, NG, false>(g, s, d_x, d_scale, d_y, partial);
   if (g.n_spans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
                        g.n_spans, g.n, d_scale, d_y);

@@ -9,11 +9,14 @@
 static inline int64_t nwc_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline int64_t nwc_round_up(int64_t a, int64_t b) { return nwc_ceil_div(a, b) * b; }
 
-// Decoder LDS of one workgroup for this header: W staged code regions (with
-// guard rows), the cross-wave row sums, the static decode table.
+// Decoder LDS of one matvec workgroup: two staged code regions per wave
+// (with guard rows; one decodes while the next fills), two sets of cross-wave
+// row sums, the static decode table.
+static inline int64_t nwc_lds_bytes_for(int64_t waves, int64_t rows_per_wave, int64_t max_rows) {
+  return 2 * (waves * (max_rows + NWC_GUARD_ROWS) * 256 + waves * rows_per_wave * 4) + NWC_LUT_BYTES;
+}
 static inline int64_t nwc_lds_bytes(const nwc_header_t *h) {
-  return (int64_t)h->waves_per_group * (h->max_rows + NWC_GUARD_ROWS) * 256 +
-         (int64_t)h->waves_per_group * h->rows_per_wave * 4 + NWC_LUT_BYTES;
+  return nwc_lds_bytes_for(h->waves_per_group, h->rows_per_wave, h->max_rows);
 }
 
 // Returns NWC_OK if `h` is a structurally valid header of this format version.

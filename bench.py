@@ -121,12 +121,115 @@ def cpu_baseline(S, C):
                       f"host PCG64 draws of the same distributions), single thread, {dt:.1f} s"}
 
 
+def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16):
+    """Qwen2.5-7B-shaped decode step: `layers` layers of 7 projections plus the
+    152064 x 3584 lm_head, all N(0, 1/sqrt(K)), encoded and resident."""
+    t0 = time.time()
+
+    def one(seed, n, k):
+        wt = S.device_normal_bf16(seed, (n, k), np.float32(C.sigma_for(k)), dev)
+        w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+        dm = nwc.DeviceMatrix(nwc.encode(w), dev)
+        return dict(dm=dm, n=n, k=k, y=torch.empty(n, dtype=torch.float32, device=dev),
+                    w_bf16=wt if with_bf16 else None,
+                    algo_bytes=dm.info["coded_bits"] / 8.0 + 2 * k + 4 * n, blob_bytes=dm.info["total_bytes"])
+
+    stack = []
+    for layer in range(layers):
+        stack.append({name: one(C.qwen25_seed(layer, idx), n, k) for idx, (name, n, k) in enumerate(C.QWEN25_7B)})
+        if layer % 7 == 6 or layer == layers - 1:
+            log(f"[bench] encoded {layer + 1}/{layers} layers ({time.time() - t0:.1f}s)")
+    head = one(C.QWEN25_LM_HEAD_SEED, C.QWEN25_7B_VOCAB, C.QWEN25_7B_HIDDEN)
+    h0 = torch.from_numpy(S.activation_bf16(C.QWEN25_X_SEED, C.QWEN25_7B_HIDDEN).view(np.int16)).to(dev)
+    return stack, head, h0.view(torch.bfloat16)
+
+
+def qwen25_step(torch, stack, head, h0, linear):
+    """One batch-1 decode step.  linear(m, x_bf16) -> fp32 output of matrix m.
+    As in the Qwen2 architecture, RMS norms (unit weight) precede attention,
+    the MLP and the lm_head; the residual stream stays fp32.  Attention at
+    context length 1 returns v for every query head (softmax over one
+    position), so each of the 4 KV heads feeds its 7 query heads."""
+    F = torch.nn.functional
+
+    def norm(h):
+        return (h * torch.rsqrt(h.square().mean() + 1e-6)).to(torch.bfloat16)
+
+    h = h0.float()
+    for L in stack:
+        hb = norm(h)
+        linear(L["q"], hb)
+        linear(L["k"], hb)
+        v = linear(L["v"], hb)
+        attn = v.to(torch.bfloat16).view(4, 1, 128).expand(4, 7, 128).reshape(-1).contiguous()
+        h = h + linear(L["o"], attn)
+        hb = norm(h)
+        act = (F.silu(linear(L["gate"], hb)) * linear(L["up"], hb)).to(torch.bfloat16)
+        h = h + linear(L["down"], act)
+    return linear(head, norm(h))
+
+
+def bench_qwen25_step(args, torch, nwc, S, C, dev):
+    stack, head, h0 = build_qwen25_step(torch, nwc, S, C, dev, args.layers or C.QWEN25_7B_LAYERS,
+                                        not args.no_bf16_baseline)
+    mats = [m for L in stack for m in L.values()] + [head]
+    F = torch.nn.functional
+
+    def nwc_linear(m, x):
+        m["dm"].matvec(x, m["y"])
+        return m["y"]
+
+    def bf16_linear(m, x):
+        return F.linear(x.view(1, -1), m["w_bf16"]).view(-1).float()
+
+    def graph_of(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    g_step = graph_of(lambda: qwen25_step(torch, stack, head, h0, nwc_linear))
+    ms = time_region(torch, g_step.replay, args.steps, args.warmup)
+    xs = {id(m): torch.zeros(m["k"], dtype=torch.bfloat16, device=dev) for m in mats}
+    g_mv = graph_of(lambda: [m["dm"].matvec(xs[id(m)], m["y"]) for m in mats])
+    ms_mv = time_region(torch, g_mv.replay, args.steps, args.warmup)
+    algo = sum(m["algo_bytes"] for m in mats)
+    out = {"metric": "Qwen2.5-7B-shaped batch-1 decode step, every linear through nwc_matvec",
+           "value": round(1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1/sqrt(K)) BF16 weights)",
+           "config": {"workload": "qwen25_7b_decode_step", "layers": len(stack), "matrices": len(mats),
+                      "batch": 1, "attention": "context length 1 stand-in (v repeated over the GQA heads)",
+                      "glue": "RMS norms (unit weight), fp32 residual, silu(gate)*up, in torch"},
+           "ms_matvecs_only": round(ms_mv, 4), "ms_glue": round(ms - ms_mv, 4),
+           "compressed_GBps_matvecs": round(algo / (ms_mv * 1e-3) / 1e9, 1),
+           "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(sum(m["blob_bytes"] for m in mats) / 1e9, 4),
+           "timing": "HIP graph replay of the whole step (glue in torch); matvecs alone in a second graph",
+           "kernel_source_hash": kernel_source_hash()}
+    if not args.no_bf16_baseline:
+        g_bf = graph_of(lambda: qwen25_step(torch, stack, head, h0, bf16_linear))
+        ms_bf = time_region(torch, g_bf.replay, args.steps, args.warmup)
+        y_nwc = qwen25_step(torch, stack, head, h0, nwc_linear)
+        y_bf = qwen25_step(torch, stack, head, h0, bf16_linear)
+        torch.cuda.synchronize()
+        rel = float((y_nwc - y_bf).norm() / y_bf.norm())
+        out["bf16_baseline"] = {"ms_per_step": round(ms_bf, 4), "tokens_per_s": round(1e3 / ms_bf, 2),
+                                "speedup_compressed_vs_bf16": round(ms_bf / ms, 4),
+                                "logits_rel_l2_vs_bf16_stack": rel,
+                                "kernel": "torch.nn.functional.linear (hipBLASLt/rocBLAS), same glue"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--layers", type=int, default=36)
+    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step"), default="qwen3_4b_layer_set")
+    ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--profile-sweeps", type=int, default=0,
@@ -147,6 +250,10 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.workload == "qwen25_7b_step":
+        bench_qwen25_step(args, torch, nwc, S, C, dev)
+        return
+    args.layers = args.layers or C.QWEN3_4B_LAYERS
     mats = build_layer_set(torch, nwc, S, C, dev, args.layers,
                            not args.no_bf16_baseline and not args.profile_sweeps)
     n_launch = len(mats)

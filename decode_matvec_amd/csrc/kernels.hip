@@ -223,6 +223,10 @@ __device__ __forceinline__ void stage_code(const Geom &g, const uint32_t *__rest
 }
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most N vector memory operations of this wave are in flight:
+// the last N issued (mantissa chunks) may still be on their way.
+template <int N>
+__device__ __forceinline__ void wait_code_copies() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Waits for this wave's loads (its LDS copies included), then a bare barrier
 // makes every wave's copies visible.
@@ -393,7 +397,14 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
 #pragma unroll
     for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
   }
-  staged_barrier();
+  // The code-row copies (and, for the first group, the decode table and the
+  // activations) were issued before the NG mantissa loads: wait for them only,
+  // so decoding the first 16 columns overlaps the later mantissa chunks (the
+  // compiler waits for each chunk at its first use).
+  wait_code_copies<FP8 ? 0 : NG>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
   bool stored = false;
   uint32_t buf = 0;
@@ -411,13 +422,13 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
 #pragma unroll
         for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
       }
-      wait_all_loads();
+      wait_code_copies<FP8 ? 0 : NG>();
     }
-    // This group's data arrived; take its mantissas before the next group's
-    // loads reuse mn.
+    // With PF, this group's mantissas arrived last iteration; copy them out
+    // before the next group's loads reuse mn.  Without PF they are used in place.
     uint4 m[NG];
 #pragma unroll
-    for (int j = 0; j < NG; ++j) m[j] = mn[j];
+    for (int j = 0; j < NG; ++j) m[j] = PF ? mn[j] : uint4{};
     if (PF && g.n_spans > 1 && grp != first) {
 #pragma unroll
       for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
@@ -432,7 +443,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
       }
     }
     Lane st{region0 + buf * region_bytes + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
-    float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
+    float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, PF ? m : mn, xv);
     a = row_sum_lanes(a, g.S);
     const bool row_lane = pl.s == g.S - 1u;
     stored = false;

@@ -243,3 +243,28 @@ def test_qwen25_7b_matrices_sampled():
         print(f"qwen2.5 layer0 {name} {n}x{k}", flush=True)
         wt, w = _device_matrix(C.qwen25_seed(0, idx), n, k, np.float32(C.sigma_for(k)))
         _check_big(wt, w, C.qwen25_seed(0, idx) + 7, nsample=32)
+
+
+def test_qwen25_step_two_layers_matches_bf16_stack():
+    # The decode step of the Qwen2.5-7B workload (two of its 28 layers plus the
+    # lm_head) through nwc_matvec and through torch's BF16 linear, same glue:
+    # every matrix is checked against the oracle elsewhere; this checks that
+    # the step wiring (fp32 outputs, BF16 inputs, GQA stand-in) agrees.
+    import bench
+    stack, head, h0 = bench.build_qwen25_step(torch, nwc, S, C, DEV, 2, True)
+    F = torch.nn.functional
+
+    def nwc_linear(m, x):
+        m["dm"].matvec(x, m["y"])
+        return m["y"]
+
+    def bf16_linear(m, x):
+        return F.linear(x.view(1, -1), m["w_bf16"]).view(-1).float()
+
+    y_nwc = bench.qwen25_step(torch, stack, head, h0, nwc_linear).clone()
+    y_bf = bench.qwen25_step(torch, stack, head, h0, bf16_linear)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y_nwc).all()
+    rel = float((y_nwc - y_bf).norm() / y_bf.norm())
+    print(f"qwen2.5 two-layer step: logits rel L2 vs BF16 stack {rel:.2e}", flush=True)
+    assert rel < 1e-2

@@ -50,10 +50,18 @@ def traffic_from_profiles(algo_bytes_per_launch: float):
     return d.get("hbm_bytes_per_launch")
 
 
-def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16):
-    mats = []
+FUSED_QWEN3 = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
+
+
+def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16, fused=False):
+    """The Qwen3-4B layer set, one compressed matrix per projection; with `fused`,
+    also the projections that share an input in a decoder layer encoded as one
+    matrix each (q||k||v and gate||up rows concatenated, one rank table), whose
+    activation is the first member's."""
+    mats, fmats = [], []
     t0 = time.time()
     for layer in range(layers):
+        dense = {}
         for idx, (name, n, k) in enumerate(C.QWEN3_4B):
             ws, xs = C.qwen3_seed(layer, idx)
             wt = S.device_normal_bf16(ws, (n, k), np.float32(C.sigma_for(k)), dev)
@@ -69,10 +77,20 @@ def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16):
                              blob_bytes=info["total_bytes"],
                              w_bf16=wt if with_bf16 else None,
                              x_bf16=xd.view(torch.bfloat16).view(1, k) if with_bf16 else None))
+            if fused:
+                dense[name] = (w, xd)
             del w
+        for fname, parts in FUSED_QWEN3 if fused else ():
+            w = np.concatenate([dense[p][0] for p in parts]) if len(parts) > 1 else dense[parts[0]][0]
+            n, k = w.shape
+            dm = nwc.DeviceMatrix(nwc.encode(w), dev)
+            fmats.append(dict(name=fname, n=n, k=k, dm=dm, x=dense[parts[0]][1],
+                              y=torch.empty(n, dtype=torch.float32, device=dev), info=dm.info,
+                              algo_bytes=dm.info["coded_bits"] / 8.0 + 2 * k + 4 * n,
+                              blob_bytes=dm.info["total_bytes"]))
         if layer % 6 == 5 or layer == layers - 1:
             log(f"[bench] encoded {layer + 1}/{layers} layers ({time.time() - t0:.1f}s)")
-    return mats
+    return mats, fmats
 
 
 def time_region(torch, fn, steps, warmup):
@@ -121,9 +139,10 @@ def cpu_baseline(S, C):
                       f"host PCG64 draws of the same distributions), single thread, {dt:.1f} s"}
 
 
-def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16):
+def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16, with_fused=False):
     """Qwen2.5-7B-shaped decode step: `layers` layers of 7 projections plus the
-    152064 x 3584 lm_head, all N(0, 1/sqrt(K)), encoded and resident."""
+    152064 x 3584 lm_head, all N(0, 1/sqrt(K)), encoded and resident; with
+    `with_fused`, also q||k||v and gate||up encoded as one matrix each."""
     t0 = time.time()
 
     def one(seed, n, k):
@@ -131,20 +150,34 @@ def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16):
         w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
         dm = nwc.DeviceMatrix(nwc.encode(w), dev)
         return dict(dm=dm, n=n, k=k, y=torch.empty(n, dtype=torch.float32, device=dev),
-                    w_bf16=wt if with_bf16 else None,
+                    w_bf16=wt if with_bf16 else None, w_host=w if with_fused else None,
+                    algo_bytes=dm.info["coded_bits"] / 8.0 + 2 * k + 4 * n, blob_bytes=dm.info["total_bytes"])
+
+    def fused(L, name, parts):
+        w = np.concatenate([L[p]["w_host"] for p in parts])
+        dm = nwc.DeviceMatrix(nwc.encode(w), dev)
+        n, k = w.shape
+        return dict(dm=dm, n=n, k=k, y=torch.empty(n, dtype=torch.float32, device=dev),
                     algo_bytes=dm.info["coded_bits"] / 8.0 + 2 * k + 4 * n, blob_bytes=dm.info["total_bytes"])
 
     stack = []
     for layer in range(layers):
-        stack.append({name: one(C.qwen25_seed(layer, idx), n, k) for idx, (name, n, k) in enumerate(C.QWEN25_7B)})
+        L = {name: one(C.qwen25_seed(layer, idx), n, k) for idx, (name, n, k) in enumerate(C.QWEN25_7B)}
+        if with_fused:
+            L["qkv"] = fused(L, "qkv", ("q", "k", "v"))
+            L["gate_up"] = fused(L, "gate_up", ("gate", "up"))
+        for m in L.values():
+            m.pop("w_host", None)
+        stack.append(L)
         if layer % 7 == 6 or layer == layers - 1:
             log(f"[bench] encoded {layer + 1}/{layers} layers ({time.time() - t0:.1f}s)")
     head = one(C.QWEN25_LM_HEAD_SEED, C.QWEN25_7B_VOCAB, C.QWEN25_7B_HIDDEN)
+    head.pop("w_host", None)
     h0 = torch.from_numpy(S.activation_bf16(C.QWEN25_X_SEED, C.QWEN25_7B_HIDDEN).view(np.int16)).to(dev)
     return stack, head, h0.view(torch.bfloat16)
 
 
-def qwen25_step(torch, stack, head, h0, linear):
+def qwen25_step(torch, stack, head, h0, linear, fused=False):
     """One batch-1 decode step.  linear(m, x_bf16) -> fp32 output of matrix m.
     As in the Qwen2 architecture, RMS norms (unit weight) precede attention,
     the MLP and the lm_head; the residual stream stays fp32.  Attention at
@@ -158,21 +191,29 @@ def qwen25_step(torch, stack, head, h0, linear):
     h = h0.float()
     for L in stack:
         hb = norm(h)
-        linear(L["q"], hb)
-        linear(L["k"], hb)
-        v = linear(L["v"], hb)
+        if fused:  # q||k||v and gate||up as one matvec each (outputs split by rows)
+            v = linear(L["qkv"], hb)[L["q"]["n"] + L["k"]["n"]:]
+        else:
+            linear(L["q"], hb)
+            linear(L["k"], hb)
+            v = linear(L["v"], hb)
         attn = v.to(torch.bfloat16).view(4, 1, 128).expand(4, 7, 128).reshape(-1).contiguous()
         h = h + linear(L["o"], attn)
         hb = norm(h)
-        act = (F.silu(linear(L["gate"], hb)) * linear(L["up"], hb)).to(torch.bfloat16)
+        if fused:
+            gu = linear(L["gate_up"], hb)
+            gate, up = gu[:L["gate"]["n"]], gu[L["gate"]["n"]:]
+        else:
+            gate, up = linear(L["gate"], hb), linear(L["up"], hb)
+        act = (F.silu(gate) * up).to(torch.bfloat16)
         h = h + linear(L["down"], act)
     return linear(head, norm(h))
 
 
 def bench_qwen25_step(args, torch, nwc, S, C, dev):
     stack, head, h0 = build_qwen25_step(torch, nwc, S, C, dev, args.layers or C.QWEN25_7B_LAYERS,
-                                        not args.no_bf16_baseline)
-    mats = [m for L in stack for m in L.values()] + [head]
+                                        not args.no_bf16_baseline, with_fused=True)
+    mats = [m for L in stack for name, m in L.items() if name not in ("qkv", "gate_up")] + [head]
     F = torch.nn.functional
 
     def nwc_linear(m, x):
@@ -196,6 +237,8 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
     xs = {id(m): torch.zeros(m["k"], dtype=torch.bfloat16, device=dev) for m in mats}
     g_mv = graph_of(lambda: [m["dm"].matvec(xs[id(m)], m["y"]) for m in mats])
     ms_mv = time_region(torch, g_mv.replay, args.steps, args.warmup)
+    g_fused = graph_of(lambda: qwen25_step(torch, stack, head, h0, nwc_linear, fused=True))
+    ms_fused = time_region(torch, g_fused.replay, args.steps, args.warmup)
     algo = sum(m["algo_bytes"] for m in mats)
     out = {"metric": "Qwen2.5-7B-shaped batch-1 decode step, every linear through nwc_matvec",
            "value": round(1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -207,6 +250,8 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
            "ms_matvecs_only": round(ms_mv, 4), "ms_glue": round(ms - ms_mv, 4),
            "compressed_GBps_matvecs": round(algo / (ms_mv * 1e-3) / 1e9, 1),
            "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(sum(m["blob_bytes"] for m in mats) / 1e9, 4),
+           "fused_projections": {"ms_per_step": round(ms_fused, 4), "tokens_per_s": round(1e3 / ms_fused, 2),
+                                 "note": "q||k||v and gate||up each one matrix (one launch), 4 launches per layer"},
            "timing": "HIP graph replay of the whole step (glue in torch); matvecs alone in a second graph",
            "kernel_source_hash": kernel_source_hash()}
     if not args.no_bf16_baseline:
@@ -254,8 +299,9 @@ def main():
         bench_qwen25_step(args, torch, nwc, S, C, dev)
         return
     args.layers = args.layers or C.QWEN3_4B_LAYERS
-    mats = build_layer_set(torch, nwc, S, C, dev, args.layers,
-                           not args.no_bf16_baseline and not args.profile_sweeps)
+    mats, fmats = build_layer_set(torch, nwc, S, C, dev, args.layers,
+                                  not args.no_bf16_baseline and not args.profile_sweeps,
+                                  fused=not args.profile_sweeps)
     n_launch = len(mats)
 
     def sweep():
@@ -322,6 +368,34 @@ def main():
                            "bits_per_weight_blob": round(group[0]["blob_bytes"] * 8 / (n * k), 4),
                            "geometry": {f: group[0]["info"][f] for f in ("cols_per_lane", "rows_per_wave", "waves_per_group", "n_spans")}}
 
+    # The same layers as a decoder runs them: projections sharing an input fused
+    # (q||k||v, gate||up), 4 launches per layer instead of 7.
+    def f_sweep():
+        for m in fmats:
+            m["dm"].matvec(m["x"], m["y"])
+
+    fg = torch.cuda.CUDAGraph()
+    f_sweep()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(fg):
+        f_sweep()
+    fms = time_region(torch, fg.replay, args.steps, args.warmup)
+    falgo = sum(m["algo_bytes"] for m in fmats)
+    f_shape = {}
+    for fname, _ in FUSED_QWEN3:
+        group = [m for m in fmats if m["name"] == fname]
+        gg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gg):
+            for m in group:
+                m["dm"].matvec(m["x"], m["y"])
+        gus = time_region(torch, gg.replay, max(3, args.steps // 2), 1) * 1e3 / len(group)
+        f_shape[fname] = {"shape": [group[0]["n"], group[0]["k"]], "us": round(gus, 3),
+                          "compressed_GBps": round(group[0]["algo_bytes"] / (gus * 1e-6) / 1e9, 1)}
+    fused = {"matvecs": len(fmats), "ms_per_sweep": round(fms, 4), "us_per_layer": round(fms * 1e3 / args.layers, 2),
+             "GBps": round(falgo / (fms * 1e-3) / 1e9, 1),
+             "hbm_frac_compressed": round(falgo / (fms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "per_shape": f_shape,
+             "note": "same weights, q||k||v and gate||up each encoded as one matrix (one launch each)"}
+
     bf16 = None
     if not args.no_bf16_baseline:
         F = torch.nn.functional
@@ -367,6 +441,7 @@ def main():
         "blob_GBps": round(blob / (ms * 1e-3) / 1e9, 1),
         "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(blob / 1e9, 4), "bf16_GB": round(bf16_bytes / 1e9, 4),
         "per_shape": per_shape, "bf16_baseline": bf16, "roofline": roof, "cpu_baseline": cpu,
+        "fused_projections": fused,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out), flush=True)

@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -351,125 +352,89 @@ __device__ __forceinline__ float row_sum_lanes(float a, uint32_t S) {
   return a;
 }
 
-// Waits until at most one vector memory operation of this wave is still in
-// flight (`one`: the row-sum store just issued) or none.
-__device__ __forceinline__ void wait_loads_keep_store(bool one) {
-  if (one)
-    asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 // Persistent workgroups: workgroup b decodes the row groups (x column spans)
 // [b*G/grid, (b+1)*G/grid) of the G = n_rowgroups * n_spans in order.  The
 // decode table (and, with one span per row, the activations) is staged once
-// per workgroup.  With PF, each group's code rows and mantissas are requested
-// while the previous group decodes (two LDS code regions per wave, two
-// mantissa register sets); without it a group's loads follow the previous
-// group's row sums.
-template <bool FP8, int NG, bool PF>
+// per workgroup; each group's code rows and mantissas load after the wave's
+// previous group.  Row sums close without a workgroup barrier: each wave
+// writes its R sums to the group's LDS slot and counts itself in with an LDS
+// atomic; the last of the W waves to arrive adds the W partials in wave order
+// (the same order whichever wave is last) and stores the rows.  Waves that
+// finish early go on to their next group.
+template <bool FP8, int NG>
 __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__restrict__ items,
                                                       const uint16_t *__restrict__ x,
                                                       const float *__restrict__ scale, float *__restrict__ y,
-                                                      float *__restrict__ partial) {
+                                                      float *__restrict__ partial, uint32_t groups_cap) {
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
+  // Dynamic LDS: one code region per wave, then groups_cap slots of W*R row
+  // sums, then groups_cap arrival counters (matvec_lds on the host sizes it).
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t n_groups = g.n_rowgroups * g.n_spans;
   const uint32_t first = (uint32_t)((uint64_t)blockIdx.x * n_groups / gridDim.x);
   const uint32_t last = (uint32_t)((uint64_t)(blockIdx.x + 1) * n_groups / gridDim.x);
-  // Dynamic LDS: (PF ? 2 : 1) code regions per wave, then two sets of W*R
-  // row sums (matvec_lds on the host sizes it the same way).
-  const uint32_t region0 = lds_addr(s_dyn) + (PF ? 2 : 1) * wave * g.region_words * 4;  // LDS byte addresses
-  const uint32_t region_bytes = g.region_words * 4;
-  float *red = (float *)(s_dyn + (PF ? 2 : 1) * g.W * g.region_words);  // after the code regions
+  const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;  // LDS byte address
+  float *red = (float *)(s_dyn + g.W * g.region_words);
+  uint32_t *arrived = (uint32_t *)(red + groups_cap * g.W * g.R);
 
   dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
-  Place pl = place(g, first, wave, lane);
+  const Place pl = place(g, first, wave, lane);
   X16 xv[NG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, pl.c0 + 16 * j, g.k);
-  uint4 mn[NG];
-  stage_code(g, items, pl.item, region0, lane);
+  uint4 m[NG];
+  stage_code(g, items, pl.item, region, lane);
   if (!FP8) {
     const uint4 *mp = mant_base(g, pl.item, lane);
 #pragma unroll
-    for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
+    for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
   }
-  // The code-row copies (and, for the first group, the decode table and the
-  // activations) were issued before the NG mantissa loads: wait for them only,
-  // so decoding the first 16 columns overlaps the later mantissa chunks (the
-  // compiler waits for each chunk at its first use).
+  for (uint32_t i = threadIdx.x; i < last - first; i += blockDim.x) arrived[i] = 0u;
+  // The code-row copies (and the decode table and activations) were issued
+  // before the NG mantissa loads: wait for them only, so decoding overlaps the
+  // mantissa transfer (the compiler waits for each chunk at its first use).
   wait_code_copies<FP8 ? 0 : NG>();
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  bool stored = false;
-  uint32_t buf = 0;
-  for (uint32_t grp = first; grp < last; ++grp, buf ^= (PF ? 1u : 0u)) {
+  for (uint32_t grp = first; grp < last; ++grp) {
     const Place cur = place(g, grp, wave, lane);
-    if (!PF && grp != first) {
-      // Single buffer: this group's loads start now, after the last group's sums.
+    if (grp != first) {
       if (g.n_spans > 1) {
 #pragma unroll
         for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
       }
-      stage_code(g, items, cur.item, region0, lane);
+      stage_code(g, items, cur.item, region, lane);
       if (!FP8) {
         const uint4 *mp = mant_base(g, cur.item, lane);
 #pragma unroll
-        for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
+        for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
       }
       wait_code_copies<FP8 ? 0 : NG>();
     }
-    // With PF, this group's mantissas arrived last iteration; copy them out
-    // before the next group's loads reuse mn.  Without PF they are used in place.
-    uint4 m[NG];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) m[j] = PF ? mn[j] : uint4{};
-    if (PF && g.n_spans > 1 && grp != first) {
-#pragma unroll
-      for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
-    }
-    if (PF && grp + 1 < last) {
-      const Place nxt = place(g, grp + 1, wave, lane);
-      stage_code(g, items, nxt.item, region0 + (buf ^ 1u) * region_bytes, lane);
-      if (!FP8) {
-        const uint4 *mp = mant_base(g, nxt.item, lane);
-#pragma unroll
-        for (int j = 0; j < NG; ++j) mn[j] = mp[j * 64];
-      }
-    }
-    Lane st{region0 + buf * region_bytes + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
-    float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, PF ? m : mn, xv);
+    Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
+    float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
     a = row_sum_lanes(a, g.S);
     const bool row_lane = pl.s == g.S - 1u;
-    stored = false;
     if (g.W == 1) {
       if (row_lane) store_row(g, cur.row, cur.span, a, scale, y, partial, FP8);
-      stored = true;
-    } else {
-      // Row sums alternate between two buffers by group parity: wave 0 may
-      // still read this group's while a faster wave writes the next group's.
-      float *rb = red + ((grp - first) & 1u) * g.W * g.R;
-      if (row_lane) rb[wave * g.R + pl.r] = a;
-      // LDS writes done, then a bare barrier: __syncthreads() would also wait
-      // for the next group's loads, issued above to overlap this decode.
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (wave == 0) {
-        if (lane < g.R) {
-          float t = 0.f;
-          for (uint32_t w = 0; w < g.W; ++w) t += rb[w * g.R + lane];
-          store_row(g, (int64_t)cur.row_group * g.R + lane, cur.span, t, scale, y, partial, FP8);
-        }
-        stored = true;
-      }
+      continue;
     }
-    if (PF && grp + 1 < last) wait_loads_keep_store(stored);
+    float *slot = red + (grp - first) * g.W * g.R;
+    if (row_lane) slot[wave * g.R + pl.r] = a;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's sums are in LDS
+    uint32_t before = 0;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(arrived + (grp - first), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before == g.W - 1 && lane < g.R) {
+      float t = 0.f;
+      for (uint32_t w = 0; w < g.W; ++w) t += slot[w * g.R + lane];
+      store_row(g, (int64_t)cur.row_group * g.R + lane, cur.span, t, scale, y, partial, FP8);
+    }
   }
 }
 
@@ -642,10 +607,12 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
 }
 
 // Dynamic LDS of a dequant workgroup: W code regions + W*R row sums; of a
-// matvec workgroup: one or two (double buffered) code regions per wave and
-// two sets of row sums.
+// matvec workgroup: W code regions, then per row group it decodes W*R row sums
+// and an arrival counter.
 size_t group_lds(const Geom &g) { return (size_t)g.W * g.region_words * 4 + (size_t)g.W * g.R * 4; }
-size_t matvec_lds(const Geom &g, bool pf) { return (pf ? 2 : 1) * (size_t)g.W * g.region_words * 4 + 2 * (size_t)g.W * g.R * 4; }
+size_t matvec_lds(const Geom &g, uint32_t groups_cap) {
+  return (size_t)g.W * g.region_words * 4 + (size_t)groups_cap * (g.W * g.R + 1) * 4;
+}
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -678,45 +645,38 @@ int resident_groups(const void *kernel, int block, size_t lds) {
 }
 
 // Persistent grid: as many workgroups as fit at once, each taking the same
-// number of groups (so no workgroup runs a round more than the others).
-// NWC_PERSIST=0 gives one workgroup per group (for comparisons).
-uint32_t matvec_grid(const Geom &g, const void *kernel, size_t lds) {
+// number of row groups (so no workgroup runs a round more than the others),
+// with at most 8 KiB of row-sum slots per workgroup.  NWC_PERSIST=0 gives one
+// workgroup per row group (for comparisons).
+struct Launch {
+  uint32_t grid, groups_cap;
+  size_t lds;
+};
+Launch matvec_launch_shape(const Geom &g, const void *kernel) {
   const uint32_t n_groups = g.n_rowgroups * g.n_spans;
   static const bool off = [] {
     const char *e = getenv("NWC_PERSIST");
     return e && e[0] == '0';
   }();
-  const int cap = off ? 0 : resident_groups(kernel, g.W * 64, lds);
-  if (cap <= 0 || (uint32_t)cap >= n_groups) return n_groups;
-  const uint32_t rounds = (n_groups + cap - 1) / cap;
-  return (n_groups + rounds - 1) / rounds;
-}
-
-// Double-buffered group loads: measured slower than single-buffered
-// persistent workgroups on every Qwen-shaped matrix (the second code region
-// halves how many workgroups fit a CU), so off unless NWC_PF=1.
-bool prefetch_groups() {
-  static const bool on = [] {
-    const char *e = getenv("NWC_PF");
-    return e && e[0] == '1';
-  }();
-  return on;
-}
-
-template <bool FP8, int NG, bool PF>
-void launch_matvec_pf(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
-  const void *kernel = (const void *)matvec_kernel<FP8, NG, PF>;
-  const size_t lds = matvec_lds(g, PF);
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG, PF>), dim3(matvec_grid(g, kernel, lds)), dim3(g.W * 64), lds, s, g,
-                     item_table(g), (const uint16_t *)d_x, d_scale, d_y, partial);
+  const uint32_t slot = (g.W * g.R + 1) * 4;
+  const uint32_t cap_slots = std::max<uint32_t>(1, 8192 / slot);
+  uint32_t grid = n_groups;
+  if (!off) {
+    const int cap = resident_groups(kernel, g.W * 64, matvec_lds(g, std::min<uint32_t>(cap_slots, 4)));
+    if (cap > 0 && (uint32_t)cap < n_groups) {
+      const uint32_t rounds = std::min<uint32_t>((n_groups + cap - 1) / cap, cap_slots);
+      grid = (n_groups + rounds - 1) / rounds;
+    }
+  }
+  const uint32_t groups_cap = (n_groups + grid - 1) / grid;
+  return Launch{grid, groups_cap, matvec_lds(g, groups_cap)};
 }
 
 template <bool FP8, int NG>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
-  if (prefetch_groups())
-    launch_matvec_pf<FP8, NG, true>(g, s, d_x, d_scale, d_y, partial);
-  else
-    launch_matvec_pf<FP8, NG, false>(g, s, d_x, d_scale, d_y, partial);
+  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG>);
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG>), dim3(L.grid), dim3(g.W * 64), L.lds, s, g, item_table(g),
+                     (const uint16_t *)d_x, d_scale, d_y, partial, L.groups_cap);
   if (g.n_spans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
                        g.n_spans, g.n, d_scale, d_y);

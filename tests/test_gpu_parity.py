@@ -251,7 +251,7 @@ def test_qwen25_step_two_layers_matches_bf16_stack():
     # every matrix is checked against the oracle elsewhere; this checks that
     # the step wiring (fp32 outputs, BF16 inputs, GQA stand-in) agrees.
     import bench
-    stack, head, h0 = bench.build_qwen25_step(torch, nwc, S, C, DEV, 2, True)
+    stack, head, h0 = bench.build_qwen25_step(torch, nwc, S, C, DEV, 2, True, with_fused=True)
     F = torch.nn.functional
 
     def nwc_linear(m, x):
@@ -262,9 +262,14 @@ def test_qwen25_step_two_layers_matches_bf16_stack():
         return F.linear(x.view(1, -1), m["w_bf16"]).view(-1).float()
 
     y_nwc = bench.qwen25_step(torch, stack, head, h0, nwc_linear).clone()
+    y_fused = bench.qwen25_step(torch, stack, head, h0, nwc_linear, fused=True).clone()
     y_bf = bench.qwen25_step(torch, stack, head, h0, bf16_linear)
     torch.cuda.synchronize()
     assert torch.isfinite(y_nwc).all()
     rel = float((y_nwc - y_bf).norm() / y_bf.norm())
-    print(f"qwen2.5 two-layer step: logits rel L2 vs BF16 stack {rel:.2e}", flush=True)
+    rel_f = float((y_fused - y_nwc).norm() / y_nwc.norm())
+    print(f"qwen2.5 two-layer step: logits rel L2 vs BF16 stack {rel:.2e}, fused vs separate {rel_f:.2e}", flush=True)
     assert rel < 1e-2
+    # q||k||v and gate||up encoded as one matrix decode the same weights; only
+    # the fp32 summation order of a row may differ.
+    assert rel_f < 1e-4

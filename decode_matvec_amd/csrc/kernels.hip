@@ -386,16 +386,8 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
   for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, pl.c0 + 16 * j, g.k);
   uint4 m[NG];
   stage_code(g, items, pl.item, region, lane);
-  if (!FP8) {
-    const uint4 *mp = mant_base(g, pl.item, lane);
-#pragma unroll
-    for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
-  }
   for (uint32_t i = threadIdx.x; i < last - first; i += blockDim.x) arrived[i] = 0u;
-  // The code-row copies (and the decode table and activations) were issued
-  // before the NG mantissa loads: wait for them only, so decoding overlaps the
-  // mantissa transfer (the compiler waits for each chunk at its first use).
-  wait_code_copies<FP8 ? 0 : NG>();
+  wait_all_loads();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -408,12 +400,17 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
         for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
       }
       stage_code(g, items, cur.item, region, lane);
-      if (!FP8) {
-        const uint4 *mp = mant_base(g, cur.item, lane);
+      wait_all_loads();
+    }
+    // Mantissas are requested only once the code rows are in: at kernel start
+    // the memory system then serves the code rows of every wave first (a third
+    // of the bytes), every wave starts decoding early, and the mantissa bytes
+    // stream in during the decode (the compiler waits for them at the
+    // multiply-adds, which it places after the decode steps).
+    if (!FP8) {
+      const uint4 *mp = mant_base(g, cur.item, lane);
 #pragma unroll
-        for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
-      }
-      wait_code_copies<FP8 ? 0 : NG>();
+      for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
     }
     Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
     float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);

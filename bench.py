@@ -268,15 +268,121 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_tied_embedding(args, torch, nwc, S, C, dev):
+    """Tied embedding / lm_head 151936 x 2560 N(0, 0.02): the lm_head GEMV (a
+    ~575 MB blob, larger than the 256 MB last-level cache, so each call reads
+    it from HBM), the gather of 4096 uniform token ids, a full dequantization;
+    and the fp8 e4m3 variant: the 1024 x 1024 matrix and 9728 x 2560 matrices."""
+    F = torch.nn.functional
+    n, k = C.EMBED_VOCAB, C.EMBED_HIDDEN
+    wt = S.device_normal_bf16(C.EMBED["w_seed"], (n, k), 0.02, dev)
+    w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+    dm = nwc.DeviceMatrix(nwc.encode(w), dev)
+    del w
+    x = torch.from_numpy(S.activation_bf16(C.EMBED["x_seed"], k).view(np.int16)).to(dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    algo = dm.info["coded_bits"] / 8.0 + 2 * k + 4 * n
+
+    def graph_of(fn):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    ms_mv = time_region(torch, graph_of(lambda: dm.matvec(x, y)).replay, args.steps, args.warmup)
+    xb = x.view(torch.bfloat16).view(1, k)
+    F.linear(xb, wt)
+    torch.cuda.synchronize()
+    ms_bf = time_region(torch, graph_of(lambda: F.linear(xb, wt)).replay, args.steps, args.warmup)
+    ids = torch.from_numpy(S.token_ids(C.EMBED["ids_seed"], n, C.N_IDS)).to(dev)
+    out = torch.empty((C.N_IDS, k), dtype=torch.int16, device=dev)
+    ms_g = time_region(torch, graph_of(lambda: dm.gather(ids, out)).replay, args.steps, args.warmup)
+    ms_emb = time_region(torch, graph_of(lambda: torch.index_select(wt, 0, ids)).replay, args.steps, args.warmup)
+    full = torch.empty((n, k), dtype=torch.int16, device=dev)
+    ms_dq = time_region(torch, graph_of(lambda: dm.dequant(full)).replay, max(2, args.steps // 4), 1)
+    del full
+
+    fp8 = {}
+    for tag, (fn_, fk, seeds) in {"single_1024": (1024, 1024, [C.SINGLE["w_seed"]]),
+                                   "gate_9728x2560": (9728, 2560, list(range(600000, 600012)))}.items():
+        dms, scs = [], []
+        for sd in seeds:
+            if fn_ == 1024:
+                wf = S.normal_bf16(sd, (fn_, fk), C.SINGLE["sigma"])
+            else:
+                wf = S.device_normal_bf16(sd, (fn_, fk), np.float32(C.sigma_for(fk)), dev)
+                wf = wf.view(torch.int16).cpu().numpy().view(np.uint16)
+            q, sc = S.fp8_quantize(wf)
+            dms.append(nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), dev))
+            scs.append(torch.from_numpy(sc).to(dev))
+        xf = torch.from_numpy(S.activation_bf16(C.SINGLE["x_seed"], fk).view(np.int16)).to(dev)
+        yf = torch.empty(fn_, dtype=torch.float32, device=dev)
+        msf = time_region(torch, graph_of(lambda: [d.matvec(xf, yf, scale=sc) for d, sc in zip(dms, scs)]).replay,
+                          args.steps, args.warmup) / len(dms)
+        fa = dms[0].info["coded_bits"] / 8.0 + 2 * fk + 4 * fn_
+        fp8[tag] = {"us": round(msf * 1e3, 3), "compressed_GBps": round(fa / (msf * 1e-3) / 1e9, 1),
+                    "bits_per_weight_coded": round(dms[0].info["coded_bits"] / (fn_ * fk), 4),
+                    "rotation": len(dms)}
+    out_j = {"metric": "tied embedding 151936x2560: lm_head GEMV, 4096-id gather, dequant; fp8 e4m3 variant",
+             "value": round(algo / (ms_mv * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+             "warmup": args.warmup, "ms_per_step": round(ms_mv, 4), "higher_is_better": True, "scaling": "weak",
+             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,0.02) BF16 weights)",
+             "config": {"workload": "tied_embedding", "vocab": n, "hidden": k, "ids": C.N_IDS},
+             "lm_head": {"us": round(ms_mv * 1e3, 2), "compressed_GBps": round(algo / (ms_mv * 1e-3) / 1e9, 1),
+                         "hbm_frac_compressed": round(algo / (ms_mv * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "blob_MB": round(dm.info["total_bytes"] / 1e6, 1),
+                         "geometry": {f: dm.info[f] for f in ("cols_per_lane", "rows_per_wave", "waves_per_group")},
+                         "bf16_F_linear_us": round(ms_bf * 1e3, 2), "speedup_vs_bf16": round(ms_bf / ms_mv, 4)},
+             "gather_4096": {"us": round(ms_g * 1e3, 2), "torch_index_select_on_bf16_us": round(ms_emb * 1e3, 2)},
+             "dequant_full": {"us": round(ms_dq * 1e3, 1),
+                              "GBps_written": round(2.0 * n * k / (ms_dq * 1e-3) / 1e9, 1)},
+             "fp8": fp8, "kernel_source_hash": kernel_source_hash()}
+    print(json.dumps(out_j), flush=True)
+
+
+def measure_fused(torch, fmats, args):
+    def f_sweep():
+        for m in fmats:
+            m["dm"].matvec(m["x"], m["y"])
+
+    fg = torch.cuda.CUDAGraph()
+    f_sweep()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(fg):
+        f_sweep()
+    fms = time_region(torch, fg.replay, args.steps, args.warmup)
+    falgo = sum(m["algo_bytes"] for m in fmats)
+    f_shape = {}
+    for fname, _ in FUSED_QWEN3:
+        group = [m for m in fmats if m["name"] == fname]
+        gg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gg):
+            for m in group:
+                m["dm"].matvec(m["x"], m["y"])
+        gus = time_region(torch, gg.replay, max(3, args.steps // 2), 1) * 1e3 / len(group)
+        f_shape[fname] = {"shape": [group[0]["n"], group[0]["k"]], "us": round(gus, 3),
+                          "compressed_GBps": round(group[0]["algo_bytes"] / (gus * 1e-6) / 1e9, 1)}
+    fused = {"matvecs": len(fmats), "ms_per_sweep": round(fms, 4), "us_per_layer": round(fms * 1e3 / args.layers, 2),
+             "GBps": round(falgo / (fms * 1e-3) / 1e9, 1),
+             "hbm_frac_compressed": round(falgo / (fms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "per_shape": f_shape,
+             "note": "same weights, q||k||v and gate||up each encoded as one matrix (one launch each)"}
+    return fused
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step"), default="qwen3_4b_layer_set")
+    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step", "tied_embedding"),
+                    default="qwen3_4b_layer_set")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-projection measurement")
     ap.add_argument("--profile-sweeps", type=int, default=0,
                     help="run this many eager sweeps and exit, untimed (for rocprofv3 counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -298,10 +404,13 @@ def main():
     if args.workload == "qwen25_7b_step":
         bench_qwen25_step(args, torch, nwc, S, C, dev)
         return
+    if args.workload == "tied_embedding":
+        bench_tied_embedding(args, torch, nwc, S, C, dev)
+        return
     args.layers = args.layers or C.QWEN3_4B_LAYERS
     mats, fmats = build_layer_set(torch, nwc, S, C, dev, args.layers,
                                   not args.no_bf16_baseline and not args.profile_sweeps,
-                                  fused=not args.profile_sweeps)
+                                  fused=not (args.profile_sweeps or args.no_fused))
     n_launch = len(mats)
 
     def sweep():
@@ -370,31 +479,7 @@ def main():
 
     # The same layers as a decoder runs them: projections sharing an input fused
     # (q||k||v, gate||up), 4 launches per layer instead of 7.
-    def f_sweep():
-        for m in fmats:
-            m["dm"].matvec(m["x"], m["y"])
-
-    fg = torch.cuda.CUDAGraph()
-    f_sweep()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(fg):
-        f_sweep()
-    fms = time_region(torch, fg.replay, args.steps, args.warmup)
-    falgo = sum(m["algo_bytes"] for m in fmats)
-    f_shape = {}
-    for fname, _ in FUSED_QWEN3:
-        group = [m for m in fmats if m["name"] == fname]
-        gg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gg):
-            for m in group:
-                m["dm"].matvec(m["x"], m["y"])
-        gus = time_region(torch, gg.replay, max(3, args.steps // 2), 1) * 1e3 / len(group)
-        f_shape[fname] = {"shape": [group[0]["n"], group[0]["k"]], "us": round(gus, 3),
-                          "compressed_GBps": round(group[0]["algo_bytes"] / (gus * 1e-6) / 1e9, 1)}
-    fused = {"matvecs": len(fmats), "ms_per_sweep": round(fms, 4), "us_per_layer": round(fms * 1e3 / args.layers, 2),
-             "GBps": round(falgo / (fms * 1e-3) / 1e9, 1),
-             "hbm_frac_compressed": round(falgo / (fms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "per_shape": f_shape,
-             "note": "same weights, q||k||v and gate||up each encoded as one matrix (one launch each)"}
+    fused = measure_fused(torch, fmats, args) if fmats else None
 
     bf16 = None
     if not args.no_bf16_baseline:

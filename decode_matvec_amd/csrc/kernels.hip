@@ -215,10 +215,10 @@ __device__ __forceinline__ void lds_store(uint32_t byte_addr, uint32_t v) { *(ld
 // Copies item `item`'s code rows into the wave's LDS region (byte address
 // `region`) and zeroes the two guard rows after them (this lane's column
 // only; the lane is the only reader of its column).
-__device__ __forceinline__ void stage_code(const Geom &g, const uint32_t *__restrict__ items, uint32_t item,
+__device__ __forceinline__ void stage_code(const uint8_t *code, const uint32_t *__restrict__ items, uint32_t item,
                                            uint32_t region, uint32_t lane) {
   const uint32_t off = items[2 * item], rows = items[2 * item + 1];
-  dma_to_lds(g.blob + g.off_code + off, region, rows * 256, lane);
+  dma_to_lds(code + off, region, rows * 256, lane);
   lds_store(region + rows * 256 + 4 * lane, 0u);
   lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
 }
@@ -328,16 +328,6 @@ __device__ __forceinline__ float slice_dot_fp8(Lane &st, const X16 (&xv)[NG]) {
 // 4 spans (16-byte loads in the reduction).
 __device__ __forceinline__ uint32_t spans_pad(uint32_t n_spans) { return (n_spans + 3u) & ~3u; }
 
-__device__ __forceinline__ void store_row(const Geom &g, int64_t row, uint32_t span, float v,
-                                          const float *__restrict__ scale, float *__restrict__ y,
-                                          float *__restrict__ partial, bool fp8) {
-  if (row >= g.n) return;
-  if (g.n_spans == 1)
-    y[row] = fp8 ? v * scale[row] : v;
-  else
-    partial[(uint64_t)row * spans_pad(g.n_spans) + span] = v;
-}
-
 // Sum of the S adjacent lanes of each row (S a power of two, 1..64), left in
 // the row's last lane (lane r*S + S-1); other lanes hold partial windows.
 // DPP adds in a fixed order: row_shr 1, 2, 4, 8 sum windows of up to 16
@@ -352,6 +342,38 @@ __device__ __forceinline__ float row_sum_lanes(float a, uint32_t S) {
   return a;
 }
 
+// Geometry of the matrix-vector product, resolved on the host: the plane
+// base pointers instead of the blob and its offsets, and 32-bit sizes (the
+// format caps n and k at 2^31).  All of it is wave-uniform and lives in scalar
+// registers, which also bound how many waves a SIMD takes.  The buffers the
+// kernel reads or writes are __restrict__ kernel arguments of their own: with
+// them the compiler may read the item table through the scalar cache.
+struct MvArgs {
+  const uint8_t *code;  // code plane
+  const uint8_t *mant;  // mantissa plane
+  const uint8_t *lut;   // decode table
+  uint32_t n, k, R, W, log2S, n_spans, n_groups, region_words, r2s_lo, r2s_hi, groups_cap;
+};
+
+// y[row] (times the fp8 row scale) with one span per row, else the span's
+// partial sum at [row][spans_pad(n_spans)].
+template <bool FP8>
+__device__ __forceinline__ void store_out(const MvArgs &a, uint32_t row, uint32_t span, float v,
+                                          const float *__restrict__ scale, float *__restrict__ y,
+                                          float *__restrict__ partial) {
+  if (row >= a.n) return;
+  if (a.n_spans == 1)
+    y[row] = FP8 ? v * scale[row] : v;
+  else
+    partial[(uint64_t)row * spans_pad(a.n_spans) + span] = v;
+}
+
+template <int NG>
+__device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uint32_t k, X16 (&xv)[NG], uint32_t c0) {
+#pragma unroll
+  for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, (int64_t)c0 + 16 * j, k);
+}
+
 // Persistent workgroups: workgroup b decodes the row groups (x column spans)
 // [b*G/grid, (b+1)*G/grid) of the G = n_rowgroups * n_spans in order.  The
 // decode table (and, with one span per row, the activations) is staged once
@@ -362,30 +384,33 @@ __device__ __forceinline__ float row_sum_lanes(float a, uint32_t S) {
 // (the same order whichever wave is last) and stores the rows.  Waves that
 // finish early go on to their next group.
 template <bool FP8, int NG>
-__global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__restrict__ items,
+__global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint32_t *__restrict__ items,
                                                       const uint16_t *__restrict__ x,
                                                       const float *__restrict__ scale, float *__restrict__ y,
-                                                      float *__restrict__ partial, uint32_t groups_cap) {
+                                                      float *__restrict__ partial) {
+  constexpr uint32_t C = 16 * NG;
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
   // Dynamic LDS: one code region per wave, then groups_cap slots of W*R row
   // sums, then groups_cap arrival counters (matvec_lds on the host sizes it).
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t n_groups = g.n_rowgroups * g.n_spans;
-  const uint32_t first = (uint32_t)((uint64_t)blockIdx.x * n_groups / gridDim.x);
-  const uint32_t last = (uint32_t)((uint64_t)(blockIdx.x + 1) * n_groups / gridDim.x);
-  const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;  // LDS byte address
-  float *red = (float *)(s_dyn + g.W * g.region_words);
-  uint32_t *arrived = (uint32_t *)(red + groups_cap * g.W * g.R);
+  const uint32_t first = (uint32_t)((uint64_t)blockIdx.x * a.n_groups / gridDim.x);
+  const uint32_t last = (uint32_t)((uint64_t)(blockIdx.x + 1) * a.n_groups / gridDim.x);
+  const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
+  float *red = (float *)(s_dyn + a.W * a.region_words);
+  uint32_t *arrived = (uint32_t *)(red + a.groups_cap * a.W * a.R);
+  const uint32_t S = 1u << a.log2S;
+  const uint32_t r = lane >> a.log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
+  const bool row_lane = (lane & (S - 1u)) == S - 1u;
 
-  dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
-  const Place pl = place(g, first, wave, lane);
+  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += a.W)
+    dma_1k(a.lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
+  // (row group, span) of the current group, stepped without a division.
+  uint32_t rg = first / a.n_spans, sp = first - rg * a.n_spans;
   X16 xv[NG];
-#pragma unroll
-  for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, pl.c0 + 16 * j, g.k);
-  uint4 m[NG];
-  stage_code(g, items, pl.item, region, lane);
+  load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
+  stage_code(a.code, items, first * a.W + wave, region, lane);
   for (uint32_t i = threadIdx.x; i < last - first; i += blockDim.x) arrived[i] = 0u;
   wait_all_loads();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -393,13 +418,10 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
   asm volatile("" ::: "memory");
 
   for (uint32_t grp = first; grp < last; ++grp) {
-    const Place cur = place(g, grp, wave, lane);
+    const uint32_t item = grp * a.W + wave;
     if (grp != first) {
-      if (g.n_spans > 1) {
-#pragma unroll
-        for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, cur.c0 + 16 * j, g.k);
-      }
-      stage_code(g, items, cur.item, region, lane);
+      if (a.n_spans > 1) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
+      stage_code(a.code, items, item, region, lane);
       wait_all_loads();
     }
     // Mantissas are requested only once the code rows are in: at kernel start
@@ -407,30 +429,34 @@ __global__ __launch_bounds__(1024) void matvec_kernel(Geom g, const uint32_t *__
     // of the bytes), every wave starts decoding early, and the mantissa bytes
     // stream in during the decode (the compiler waits for them at the
     // multiply-adds, which it places after the decode steps).
+    uint4 m[NG];
     if (!FP8) {
-      const uint4 *mp = mant_base(g, cur.item, lane);
+      const uint4 *mp = (const uint4 *)(a.mant + (uint64_t)item * (64 * C)) + lane;
 #pragma unroll
       for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
     }
-    Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
-    float a = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
-    a = row_sum_lanes(a, g.S);
-    const bool row_lane = pl.s == g.S - 1u;
-    if (g.W == 1) {
-      if (row_lane) store_row(g, cur.row, cur.span, a, scale, y, partial, FP8);
-      continue;
+    Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};
+    float v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
+    v = row_sum_lanes(v, S);
+    if (a.W == 1) {
+      if (row_lane) store_out<FP8>(a, rg * a.R + r, sp, v, scale, y, partial);
+    } else {
+      float *slot = red + (grp - first) * a.W * a.R;
+      if (row_lane) slot[wave * a.R + r] = v;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's sums are in LDS
+      uint32_t before = 0;
+      if (lane == 0)
+        before = __hip_atomic_fetch_add(arrived + (grp - first), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      before = __builtin_amdgcn_readfirstlane(before);
+      if (before == a.W - 1 && lane < a.R) {
+        float t = 0.f;
+        for (uint32_t w = 0; w < a.W; ++w) t += slot[w * a.R + lane];
+        store_out<FP8>(a, rg * a.R + lane, sp, t, scale, y, partial);
+      }
     }
-    float *slot = red + (grp - first) * g.W * g.R;
-    if (row_lane) slot[wave * g.R + pl.r] = a;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's sums are in LDS
-    uint32_t before = 0;
-    if (lane == 0)
-      before = __hip_atomic_fetch_add(arrived + (grp - first), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    before = __builtin_amdgcn_readfirstlane(before);
-    if (before == g.W - 1 && lane < g.R) {
-      float t = 0.f;
-      for (uint32_t w = 0; w < g.W; ++w) t += slot[w * g.R + lane];
-      store_row(g, (int64_t)cur.row_group * g.R + lane, cur.span, t, scale, y, partial, FP8);
+    if (++sp == a.n_spans) {
+      sp = 0;
+      ++rg;
     }
   }
 }
@@ -522,7 +548,7 @@ __global__ __launch_bounds__(1024) void dequant_kernel(Geom g, const uint32_t *_
   const Place pl = place(g, blockIdx.x, wave, lane);
   const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
   dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
-  stage_code(g, items, pl.item, region, lane);
+  stage_code(g.blob + g.off_code, items, pl.item, region, lane);
   staged_barrier();
   Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
   const int64_t esz = FP8 ? 1 : 2;
@@ -672,8 +698,23 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel) {
 template <bool FP8, int NG>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
   const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG>);
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG>), dim3(L.grid), dim3(g.W * 64), L.lds, s, g, item_table(g),
-                     (const uint16_t *)d_x, d_scale, d_y, partial, L.groups_cap);
+  MvArgs a;
+  a.code = g.blob + g.off_code;
+  a.mant = g.blob + g.off_mant;
+  a.lut = g.blob + g.off_lut;
+  a.n = (uint32_t)g.n;
+  a.k = (uint32_t)g.k;
+  a.R = g.R;
+  a.W = g.W;
+  a.log2S = g.log2S;
+  a.n_spans = g.n_spans;
+  a.n_groups = g.n_rowgroups * g.n_spans;
+  a.region_words = g.region_words;
+  a.r2s_lo = g.r2s_lo;
+  a.r2s_hi = g.r2s_hi;
+  a.groups_cap = L.groups_cap;
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG>), dim3(L.grid), dim3(g.W * 64), L.lds, s, a, item_table(g),
+                     (const uint16_t *)d_x, d_scale, d_y, partial);
   if (g.n_spans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
                        g.n_spans, g.n, d_scale, d_y);

@@ -98,7 +98,7 @@ __device__ __forceinline__ void bf16_code(uint32_t v, uint32_t lo, uint32_t hi, 
 }
 
 // Two BF16 codes at bit Q+2, in the decode table's entry format (slow path).
-__device__ __noinline__ uint32_t bf16_pair_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
+__device__ __forceinline__ uint32_t bf16_pair_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
   const uint64_t v = window64(col_base, Q + NWC_LEAD_BITS);
   uint32_t ha, la, hb, lb;
   bf16_code((uint32_t)v, lo, hi, ha, la);
@@ -118,7 +118,7 @@ __device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t b) {
 }
 
 // One fp8 code at bit Q+2, in the decode table's entry format (slow path).
-__device__ __noinline__ uint32_t fp8_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
+__device__ __forceinline__ uint32_t fp8_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
   const uint32_t v = (uint32_t)window64(col_base, Q + NWC_LEAD_BITS);
   const uint32_t r = __builtin_ctz(~v | 0x100u);
   uint32_t s, E, M, len;
@@ -224,6 +224,45 @@ __device__ __forceinline__ void stage_code(const uint8_t *code, const uint32_t *
 }
 
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same waits as builtins, which the compiler's own wait placement takes
+// into account (it does not read inline assembly): vmcnt(0), lgkmcnt(0).
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Buffer resource word 3 for untyped 32-bit accesses (data format 32).
+constexpr int kBufWord3 = 0x00020000;
+
+// The first PR code rows of an item, this lane's column, fetched into
+// registers while the wave still decodes its previous item.  The loads go
+// through a buffer resource sized to the item (rows * 256 bytes): rows past the
+// item's end read as zero without a memory access and become its guard rows.
+// rows == 0 fetches nothing (no next item).
+template <int PR>
+__device__ __forceinline__ void fetch_code_ahead(const uint8_t *code, uint32_t off, uint32_t rows, uint32_t lane,
+                                                 uint32_t (&w)[PR]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(code + off), (short)0, (int)(rows * 256), kBufWord3);
+#pragma unroll
+  for (int j = 0; j < PR; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, j * 256 + 4 * lane, 0, 0);
+}
+
+// Puts a fetched item into the wave's LDS region: the PR register rows (the
+// rows the region holds), then, for an item longer than PR - 2 rows, its other
+// rows straight from memory and the two zero guard rows.
+template <int PR>
+__device__ __forceinline__ void commit_code_ahead(const uint8_t *code, uint32_t off, uint32_t rows,
+                                                  uint32_t region_rows, uint32_t region, uint32_t lane,
+                                                  const uint32_t (&w)[PR]) {
+#pragma unroll
+  for (int j = 0; j < PR; ++j)
+    if ((uint32_t)j < region_rows) lds_store(region + j * 256 + 4 * lane, w[j]);
+  if (rows + NWC_GUARD_ROWS > (uint32_t)PR) {
+    if (rows > (uint32_t)PR) dma_to_lds(code + off + PR * 256, region + PR * 256, (rows - PR) * 256, lane);
+    lds_store(region + rows * 256 + 4 * lane, 0u);
+    lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
+    wait_vm0();
+  }
+}
 // Waits until at most N vector memory operations of this wave are in flight:
 // the last N issued (mantissa chunks) may still be on their way.
 template <int N>
@@ -377,29 +416,29 @@ __device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uin
 // Persistent workgroups: workgroup b decodes the row groups (x column spans)
 // [b*G/grid, (b+1)*G/grid) of the G = n_rowgroups * n_spans in order.  The
 // decode table (and, with one span per row, the activations) is staged once
-// per workgroup; each group's code rows and mantissas load after the wave's
-// previous group.  Row sums close without a workgroup barrier: each wave
-// writes its R sums to the group's LDS slot and counts itself in with an LDS
-// atomic; the last of the W waves to arrive adds the W partials in wave order
-// (the same order whichever wave is last) and stores the rows.  Waves that
-// finish early go on to their next group.
+// per workgroup.  Each wave fetches the code rows of its next item into
+// registers while it decodes the current one, so after the first item the
+// memory system streams while the waves decode.  Row sums go to per-group LDS
+// slots; the outputs are written once every wave is done, each row adding its
+// W wave partials in wave order.
 template <bool FP8, int NG>
 __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint32_t *__restrict__ items,
                                                       const uint16_t *__restrict__ x,
                                                       const float *__restrict__ scale, float *__restrict__ y,
                                                       float *__restrict__ partial) {
   constexpr uint32_t C = 16 * NG;
+  constexpr int PR = 2 * NG + 2;  // code rows fetched ahead (an item's rows and its guard rows, typically)
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
   // Dynamic LDS: one code region per wave, then groups_cap slots of W*R row
-  // sums, then groups_cap arrival counters (matvec_lds on the host sizes it).
+  // sums (matvec_lds on the host sizes it).
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t first = (uint32_t)((uint64_t)blockIdx.x * a.n_groups / gridDim.x);
   const uint32_t last = (uint32_t)((uint64_t)(blockIdx.x + 1) * a.n_groups / gridDim.x);
   const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
+  const uint32_t region_rows = a.region_words >> 6;
   float *red = (float *)(s_dyn + a.W * a.region_words);
-  uint32_t *arrived = (uint32_t *)(red + a.groups_cap * a.W * a.R);
   const uint32_t S = 1u << a.log2S;
   const uint32_t r = lane >> a.log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
   const bool row_lane = (lane & (S - 1u)) == S - 1u;
@@ -411,53 +450,53 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   X16 xv[NG];
   load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
   stage_code(a.code, items, first * a.W + wave, region, lane);
-  for (uint32_t i = threadIdx.x; i < last - first; i += blockDim.x) arrived[i] = 0u;
-  wait_all_loads();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  wait_vm0();
+  wait_lgkm0();
   __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 
+  uint32_t ahead[PR];
   for (uint32_t grp = first; grp < last; ++grp) {
     const uint32_t item = grp * a.W + wave;
     if (grp != first) {
       if (a.n_spans > 1) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
-      stage_code(a.code, items, item, region, lane);
-      wait_all_loads();
+      commit_code_ahead<PR>(a.code, items[2 * item], items[2 * item + 1], region_rows, region, lane, ahead);
     }
-    // Mantissas are requested only once the code rows are in: at kernel start
-    // the memory system then serves the code rows of every wave first (a third
-    // of the bytes), every wave starts decoding early, and the mantissa bytes
-    // stream in during the decode (the compiler waits for them at the
-    // multiply-adds, which it places after the decode steps).
+    // Mantissas of this item, then the next item's code rows: the decode below
+    // reads only LDS, so both stream in while it runs (the compiler waits for
+    // the mantissas at the multiply-adds, which it places after the decode
+    // steps, and for the code rows at the next commit).
     uint4 m[NG];
     if (!FP8) {
       const uint4 *mp = (const uint4 *)(a.mant + (uint64_t)item * (64 * C)) + lane;
 #pragma unroll
       for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
     }
+    {
+      const bool more = grp + 1 < last;
+      const uint32_t nx = more ? item + a.W : item;
+      fetch_code_ahead<PR>(a.code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
+    }
     Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};
     float v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
     v = row_sum_lanes(v, S);
-    if (a.W == 1) {
-      if (row_lane) store_out<FP8>(a, rg * a.R + r, sp, v, scale, y, partial);
-    } else {
-      float *slot = red + (grp - first) * a.W * a.R;
-      if (row_lane) slot[wave * a.R + r] = v;
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's sums are in LDS
-      uint32_t before = 0;
-      if (lane == 0)
-        before = __hip_atomic_fetch_add(arrived + (grp - first), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      before = __builtin_amdgcn_readfirstlane(before);
-      if (before == a.W - 1 && lane < a.R) {
-        float t = 0.f;
-        for (uint32_t w = 0; w < a.W; ++w) t += slot[w * a.R + lane];
-        store_out<FP8>(a, rg * a.R + lane, sp, t, scale, y, partial);
-      }
-    }
+    if (row_lane) red[((grp - first) * a.W + wave) * a.R + r] = v;
     if (++sp == a.n_spans) {
       sp = 0;
       ++rg;
     }
+  }
+
+  // Outputs: row (group i, r) = sum over waves w of slot[i][w][r], w ascending.
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  const uint32_t n_out = (last - first) * a.R;
+  for (uint32_t t = threadIdx.x; t < n_out; t += blockDim.x) {
+    const uint32_t i = t / a.R, rr = t - i * a.R;
+    const float *slot = red + i * a.W * a.R + rr;
+    float sum = 0.f;
+    for (uint32_t w = 0; w < a.W; ++w) sum += slot[w * a.R];
+    const uint32_t grp = first + i, grow = grp / a.n_spans;
+    store_out<FP8>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial);
   }
 }
 
@@ -630,11 +669,10 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
 }
 
 // Dynamic LDS of a dequant workgroup: W code regions + W*R row sums; of a
-// matvec workgroup: W code regions, then per row group it decodes W*R row sums
-// and an arrival counter.
+// matvec workgroup: W code regions, then per row group it decodes W*R row sums.
 size_t group_lds(const Geom &g) { return (size_t)g.W * g.region_words * 4 + (size_t)g.W * g.R * 4; }
 size_t matvec_lds(const Geom &g, uint32_t groups_cap) {
-  return (size_t)g.W * g.region_words * 4 + (size_t)groups_cap * (g.W * g.R + 1) * 4;
+  return (size_t)g.W * g.region_words * 4 + (size_t)groups_cap * g.W * g.R * 4;
 }
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -681,7 +719,7 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel) {
     const char *e = getenv("NWC_PERSIST");
     return e && e[0] == '0';
   }();
-  const uint32_t slot = (g.W * g.R + 1) * 4;
+  const uint32_t slot = g.W * g.R * 4;
   const uint32_t cap_slots = std::max<uint32_t>(1, 8192 / slot);
   uint32_t grid = n_groups;
   if (!off) {

@@ -396,12 +396,12 @@ struct MvArgs {
 
 // y[row] (times the fp8 row scale) with one span per row, else the span's
 // partial sum at [row][spans_pad(n_spans)].
-template <bool FP8>
+template <bool FP8, bool SPLIT>
 __device__ __forceinline__ void store_out(const MvArgs &a, uint32_t row, uint32_t span, float v,
                                           const float *__restrict__ scale, float *__restrict__ y,
                                           float *__restrict__ partial) {
   if (row >= a.n) return;
-  if (a.n_spans == 1)
+  if (!SPLIT)
     y[row] = FP8 ? v * scale[row] : v;
   else
     partial[(uint64_t)row * spans_pad(a.n_spans) + span] = v;
@@ -421,7 +421,7 @@ __device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uin
 // memory system streams while the waves decode.  Row sums go to per-group LDS
 // slots; the outputs are written once every wave is done, each row adding its
 // W wave partials in wave order.
-template <bool FP8, int NG>
+template <bool FP8, int NG, bool SPLIT>
 __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint32_t *__restrict__ items,
                                                       const uint16_t *__restrict__ x,
                                                       const float *__restrict__ scale, float *__restrict__ y,
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += a.W)
     dma_1k(a.lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
   // (row group, span) of the current group, stepped without a division.
-  uint32_t rg = first / a.n_spans, sp = first - rg * a.n_spans;
+  uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   X16 xv[NG];
   load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
   stage_code(a.code, items, first * a.W + wave, region, lane);
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   for (uint32_t grp = first; grp < last; ++grp) {
     const uint32_t item = grp * a.W + wave;
     if (grp != first) {
-      if (a.n_spans > 1) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
+      if (SPLIT) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
       commit_code_ahead<PR>(a.code, items[2 * item], items[2 * item + 1], region_rows, region, lane, ahead);
     }
     // Mantissas of this item, then the next item's code rows: the decode below
@@ -480,7 +480,9 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
     float v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
     v = row_sum_lanes(v, S);
     if (row_lane) red[((grp - first) * a.W + wave) * a.R + r] = v;
-    if (++sp == a.n_spans) {
+    if (!SPLIT) {
+      ++rg;
+    } else if (++sp == a.n_spans) {
       sp = 0;
       ++rg;
     }
@@ -489,14 +491,15 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   // Outputs: row (group i, r) = sum over waves w of slot[i][w][r], w ascending.
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
-  const uint32_t n_out = (last - first) * a.R;
+  const uint32_t log2R = 6 - a.log2S;
+  const uint32_t n_out = (last - first) << log2R;
   for (uint32_t t = threadIdx.x; t < n_out; t += blockDim.x) {
-    const uint32_t i = t / a.R, rr = t - i * a.R;
+    const uint32_t i = t >> log2R, rr = t & (a.R - 1u);
     const float *slot = red + i * a.W * a.R + rr;
     float sum = 0.f;
     for (uint32_t w = 0; w < a.W; ++w) sum += slot[w * a.R];
-    const uint32_t grp = first + i, grow = grp / a.n_spans;
-    store_out<FP8>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial);
+    const uint32_t grp = first + i, grow = SPLIT ? grp / a.n_spans : grp;
+    store_out<FP8, SPLIT>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial);
   }
 }
 
@@ -733,9 +736,9 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel) {
   return Launch{grid, groups_cap, matvec_lds(g, groups_cap)};
 }
 
-template <bool FP8, int NG>
+template <bool FP8, int NG, bool SPLIT>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
-  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG>);
+  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT>);
   MvArgs a;
   a.code = g.blob + g.off_code;
   a.mant = g.blob + g.off_mant;
@@ -751,7 +754,7 @@ void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d
   a.r2s_lo = g.r2s_lo;
   a.r2s_hi = g.r2s_hi;
   a.groups_cap = L.groups_cap;
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG>), dim3(L.grid), dim3(g.W * 64), L.lds, s, a, item_table(g),
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT>), dim3(L.grid), dim3(g.W * 64), L.lds, s, a, item_table(g),
                      (const uint16_t *)d_x, d_scale, d_y, partial);
   if (g.n_spans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
@@ -761,11 +764,20 @@ void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d
 template <bool FP8>
 void launch_matvec_c(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y,
                      float *partial) {
+  if (g.n_spans > 1) {
+    switch (g.C) {
+      case 16: launch_matvec<FP8, 1, true>(g, s, d_x, d_scale, d_y, partial); break;
+      case 32: launch_matvec<FP8, 2, true>(g, s, d_x, d_scale, d_y, partial); break;
+      case 48: launch_matvec<FP8, 3, true>(g, s, d_x, d_scale, d_y, partial); break;
+      default: launch_matvec<FP8, 4, true>(g, s, d_x, d_scale, d_y, partial); break;
+    }
+    return;
+  }
   switch (g.C) {
-    case 16: launch_matvec<FP8, 1>(g, s, d_x, d_scale, d_y, partial); break;
-    case 32: launch_matvec<FP8, 2>(g, s, d_x, d_scale, d_y, partial); break;
-    case 48: launch_matvec<FP8, 3>(g, s, d_x, d_scale, d_y, partial); break;
-    default: launch_matvec<FP8, 4>(g, s, d_x, d_scale, d_y, partial); break;
+    case 16: launch_matvec<FP8, 1, false>(g, s, d_x, d_scale, d_y, partial); break;
+    case 32: launch_matvec<FP8, 2, false>(g, s, d_x, d_scale, d_y, partial); break;
+    case 48: launch_matvec<FP8, 3, false>(g, s, d_x, d_scale, d_y, partial); break;
+    default: launch_matvec<FP8, 4, false>(g, s, d_x, d_scale, d_y, partial); break;
   }
 }
 

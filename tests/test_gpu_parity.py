@@ -92,6 +92,46 @@ def test_row_over_two_workgroups():
     assert dm.info["n_spans"] == 2
 
 
+def test_repeated_calls_and_graph_replays():
+    # A persistent grid with more row groups than resident workgroups: calls in
+    # a row and graph replays give the bits of the first call (the summation
+    # order is fixed), and two matrices may share one workspace in a stream.
+    w1 = S.normal_bf16(51, (9728, 2560), 0.02)
+    w2 = S.normal_bf16(52, (200, 66000), 0.02)
+    x1, x2 = S.activation_bf16(53, 2560), S.activation_bf16(54, 66000)
+    d1 = nwc.DeviceMatrix(nwc.encode(w1), DEV)
+    d2 = nwc.DeviceMatrix(nwc.encode(w2, cols_per_lane=64, rows_per_wave=1), DEV)
+    assert d1.info["n_items"] // d1.info["waves_per_group"] > 2000 and d2.info["n_spans"] == 2
+    t1, t2 = dev16(x1), dev16(x2)
+    y1 = torch.empty(d1.n, dtype=torch.float32, device=DEV)
+    y2 = torch.empty(d2.n, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(max(1, nwc.workspace_size(d2.header) // 4), dtype=torch.int32, device=DEV)
+    nwc.matvec(d1.header, d1.d_blob, t1, y1, ws)
+    nwc.matvec(d2.header, d2.d_blob, t2, y2, ws)
+    torch.cuda.synchronize()
+    ref1, ref2 = y1.cpu().numpy().copy(), y2.cpu().numpy().copy()
+    y_ref, A = O.matvec_bf16_ref(w2, x2)
+    check_tol(ref2.astype(np.float64), y_ref, A, "two spans")
+    rows = np.unique(np.random.default_rng(55).integers(0, 9728, 200))
+    y_ref, A = O.matvec_bf16_ref(w1[rows], x1)
+    check_tol(ref1[rows].astype(np.float64), y_ref, A, "persistent grid")
+    for _ in range(3):
+        nwc.matvec(d1.header, d1.d_blob, t1, y1, ws)
+        nwc.matvec(d2.header, d2.d_blob, t2, y2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1.cpu().numpy(), ref1) and np.array_equal(y2.cpu().numpy(), ref2)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nwc.matvec(d1.header, d1.d_blob, t1, y1, ws)
+        nwc.matvec(d2.header, d2.d_blob, t2, y2, ws)
+    for _ in range(3):
+        y1.fill_(float("nan"))
+        y2.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y1.cpu().numpy(), ref1) and np.array_equal(y2.cpu().numpy(), ref2)
+
+
 def test_fillers_when_rank0_is_the_top_symbol():
     # Most weights have exponent symbol 0x7F, so rank 0 is 0x7F and a filler
     # (zero code bits, zero mantissa) decodes to 0x7F00 = 2^127: finite, and

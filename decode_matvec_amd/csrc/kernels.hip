@@ -242,8 +242,12 @@ __device__ __forceinline__ void fetch_code_ahead(const uint8_t *code, uint32_t o
                                                  uint32_t (&w)[PR]) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)(code + off), (short)0, (int)(rows * 256), kBufWord3);
+  // Keeps the row offsets in the instructions' offset fields instead of one
+  // register per row (the compiler would hoist the sums out of the loop).
+  uint32_t col = 4 * lane;
+  asm volatile("" : "+v"(col));
 #pragma unroll
-  for (int j = 0; j < PR; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, j * 256 + 4 * lane, 0, 0);
+  for (int j = 0; j < PR; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, col + j * 256, 0, 0);
 }
 
 // Puts a fetched item into the wave's LDS region: the PR register rows (the

@@ -182,26 +182,30 @@ double wave_penalty(int W) { return 1.0 + 0.04 * std::max(0, W - 5) + 0.05 * std
 Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req, const RowEstimate &est) {
   std::vector<int> Cs, Rs;
   if (C_req) Cs = {C_req};
-  else if (n * k < ((int64_t)1 << 23)) Cs = {16, 32, 48, 64};
-  else Cs = {32, 48, 64};
+  else Cs = {16, 32, 48, 64};
   if (R_req) Rs = {R_req};
   else Rs = {64, 32, 16, 8, 4, 2, 1};
+  // Measured on MI355X (Qwen-shaped matrices, cold cache): 16 columns per lane
+  // is fastest up to ~2^25 weights (more, shorter items pipeline better), 32
+  // above (per-item overheads add up); 48 and 64 only where nothing else fits.
+  const double nk = (double)n * (double)k;
+  auto c_factor = [&](int C) { return C == 16 ? (nk <= (double)(1 << 25) ? 1.0 : 1.15) : C == 32 ? 1.0 : 1.25; };
+  Geo best;
+  double best_cost = 0;
   for (int C : Cs) {
-    Geo best;
-    double best_cost = 0;
     for (int R : Rs) {
       const Geo g = make_geo(n, k, C, R, NWC_MAX_WAVES);
       if (C_req && R_req) return g;
       if (g.n_spans != 1) continue;
       if (nwc_lds_bytes_for(g.W, g.R, est.rows(C)) > NWC_LDS_BUDGET) continue;
-      const double cost = (double)g.lane_cols() * wave_penalty(g.W);
-      if (!best.C || cost < best_cost) {
+      const double cost = (double)g.lane_cols() * wave_penalty(g.W) * c_factor(C);
+      if (!best.C || cost < best_cost) {  // ties keep the smaller C, then the larger R
         best = g;
         best_cost = cost;
       }
     }
-    if (best.C) return best;
   }
+  if (best.C) return best;
   return make_geo(n, k, Cs.back(), R_req ? R_req : 1, NWC_MAX_WAVES);  // k > 65536: several spans
 }
 

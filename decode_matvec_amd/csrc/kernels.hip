@@ -42,6 +42,7 @@
 
 namespace {
 
+constexpr int kWavesPerCu = 25;  // persistent grids: waves per compute unit
 constexpr uint32_t kSelLo = 0x05010400u;   // {m[0], hiA, m[1], hiB}
 constexpr uint32_t kSelHi = 0x05030402u;   // {m[2], hiA, m[3], hiB}
 constexpr uint32_t kSelPair = 0x05040100u; // {a.b0, a.b1, b.b0, b.b1}
@@ -695,7 +696,11 @@ int read_header(const void *header, nwc_header_t &h) {
 const uint32_t *item_table(const Geom &g) { return (const uint32_t *)(g.blob + g.off_items); }
 
 // Workgroups a launch keeps resident at once on this device (occupancy
-// query, cached per kernel, block size and LDS), times the compute units.
+// query, cached per kernel, block size and LDS), times the compute units; at
+// most 25 waves per compute unit.  Measured on MI355X: the query allows
+// 6 workgroups of 5 waves (30 waves) per CU for the matvec, but grids sized
+// so run slower than ones of 25 waves per CU (some workgroups then start only
+// when others finish).
 int resident_groups(const void *kernel, int block, size_t lds) {
   static std::mutex mu;
   static std::map<std::tuple<int, const void *, int, size_t>, int> cache;
@@ -709,6 +714,7 @@ int resident_groups(const void *kernel, int block, size_t lds) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
+  per_cu = std::min(per_cu, std::max(1, kWavesPerCu / (block / 64)));
   return cache[key] = per_cu * cus;
 }
 

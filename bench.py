@@ -372,6 +372,99 @@ def measure_fused(torch, fmats, args):
     return fused
 
 
+# ------------------------------------------------------------- profile summaries
+# Host-only helpers that turn rocprofv3 CSV output of this script into the
+# committed summaries under profiles/ (no GPU, no torch).
+
+def _short_kernel(name: str) -> str:
+    return name.replace("void (anonymous namespace)::", "").split("((anonymous")[0]
+
+
+def summarize_traffic(fetch_csv, write_csv, profile_json, cmd_fetch, cmd_write):
+    """FETCH_SIZE / WRITE_SIZE runs of `--profile-sweeps N --copy-calibration` -> HBM bytes per matvec
+    dispatch, each counter scaled so that it reads the calibration copy's true size."""
+    import csv
+    import statistics
+    meta = json.loads(open(profile_json).read().strip().splitlines()[-1])
+    true_kib = meta["copy_calibration_bytes"] / 1024.0
+    res = {}
+    for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == cname]
+        first_mv = min(int(r["Dispatch_Id"]) for r in rows if "matvec_kernel" in r["Kernel_Name"])
+        copies = [r for r in rows if int(r["Dispatch_Id"]) < first_mv and "copy" in r["Kernel_Name"].lower()]
+        cal = max(float(r["Counter_Value"]) for r in copies)
+        mv = [float(r["Counter_Value"]) for r in rows if "matvec_kernel" in r["Kernel_Name"]]
+        res[cname] = {"scale": true_kib / cal, "cal_kib": cal, "dispatches": len(mv),
+                      "mean_kib": statistics.mean(mv), "bytes": statistics.mean(mv) * 1024 * true_kib / cal}
+    hbm = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
+    algo, blob = meta["algo_bytes_per_matvec"], meta["blob_bytes_per_matvec"]
+    d = {"kernel_source_hash": meta["kernel_source_hash"], "hbm_bytes_per_launch": round(hbm, 1),
+         "fetch_bytes_per_launch": round(res["FETCH_SIZE"]["bytes"], 1),
+         "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes"], 1),
+         "fetch_scale": round(res["FETCH_SIZE"]["scale"], 4), "write_scale": round(res["WRITE_SIZE"]["scale"], 4),
+         "algo_bytes_per_launch": round(algo, 1), "blob_bytes_per_launch": round(blob, 1),
+         "dispatches": res["FETCH_SIZE"]["dispatches"]}
+    json.dump(d, open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.json"), "w"), indent=1)
+    with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.md"), "w") as f:
+        f.write("# matvec kernel HBM traffic, Qwen3-4B layer set (252 matvecs), MI355X\n\n"
+                "Commands (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT`):\n\n"
+                f"    {cmd_fetch}\n    {cmd_write}\n\nSummarised with `python bench.py --summarize-traffic` "
+                "(the counter CSVs and the JSON line the profiled run printed).\n\n"
+                f"Kernel source hash: {meta['kernel_source_hash']}\n\n"
+                "Counters are KiB per dispatch.  Each is scaled by the factor that maps its reading for the\n"
+                "256 MiB device-to-device calibration copy in the same run to the copy's true size.\n\n"
+                "| counter | calibration copy (KiB read) | true KiB | scale | matvec dispatches | mean KiB/dispatch | "
+                "scaled bytes/dispatch |\n|---|---|---|---|---|---|---|\n")
+        for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+            r = res[cname]
+            f.write(f"| {cname} | {r['cal_kib']:.0f} | {true_kib:.0f} | {r['scale']:.3f} | {r['dispatches']} | "
+                    f"{r['mean_kib']:.1f} | {r['bytes']:.0f} |\n")
+        f.write(f"\nPer matvec (mean over the layer set): HBM traffic {hbm / 1e6:.3f} MB; algorithmic bytes "
+                f"(coded bits/8 + 2K + 4N) {algo / 1e6:.3f} MB; blob bytes {blob / 1e6:.3f} MB.\n"
+                f"Traffic / algorithmic = {hbm / algo:.3f}; traffic / blob = {hbm / blob:.3f}.\n")
+    print(json.dumps(d, indent=1))
+
+
+def summarize_trace(prof_dir, bench_json, cmd):
+    """Kernel-trace run of the layer set -> per-kernel and per-launch-shape durations."""
+    import collections
+    import csv
+    import statistics
+    stats = list(csv.DictReader(open(os.path.join(prof_dir, "run_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(prof_dir, "run_kernel_trace.csv"))))
+    d = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    by = collections.defaultdict(list)
+    for r in trace:
+        if "matvec_kernel" in r["Kernel_Name"]:
+            key = (_short_kernel(r["Kernel_Name"]), r.get("Grid_Size") or r.get("Grid_Size_X"),
+                   r.get("Workgroup_Size") or r.get("Workgroup_Size_X"))
+            by[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mv = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if "matvec_kernel" in r["Kernel_Name"]]
+    with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_kernel_trace.md"), "w") as f:
+        f.write("# matvec kernel trace -- Qwen3-4B layer set (36 layers x 7 matrices), MI355X\n\n"
+                "Command (repo root on the GPU box):\n\n    cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT\n"
+                f"    {cmd}\n\nSummarised with `python bench.py --summarize-trace`.\n\n"
+                f"Kernel source hash: {d['kernel_source_hash']}\n\n"
+                "`run_kernel_stats.csv`, matvec rows (copy and `at::native` kernels are input set-up outside "
+                "the timed region):\n\n| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n")
+        for r in stats:
+            if "matvec_kernel" in r["Name"] or "reduce_kernel" in r["Name"]:
+                f.write(f"| {_short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                        f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |\n")
+        f.write(f"\nAll matvec dispatches: {len(mv)}, mean {statistics.mean(mv) / 1e3:.3f} us (kernel execution "
+                "only; the bench's HIP events also count the gaps between graph nodes).\n\n"
+                "Per launch shape from `run_kernel_trace.csv` (grid = threads; template arguments "
+                "<fp8, 16-column groups per lane, split rows>):\n\n"
+                "| kernel | grid | block | dispatches | median us | mean us |\n|---|---|---|---|---|---|\n")
+        for (nm, gs, ws), v in sorted(by.items(), key=lambda kv: -statistics.mean(kv[1])):
+            f.write(f"| {nm} | {gs} | {ws} | {len(v)} | {statistics.median(v) / 1e3:.2f} | {statistics.mean(v) / 1e3:.2f} |\n")
+        keep = {k: d.get(k) for k in ("value", "unit", "ms_per_step", "us_per_layer", "us_per_matvec_avg",
+                                      "roofline", "cpu_baseline", "bf16_baseline")}
+        keep["per_shape_us"] = {k: v["us"] for k, v in d["per_shape"].items()}
+        f.write("\nThe JSON line of the profiled run (its HIP events time the graph-replayed sweep, launch gaps "
+                f"included: {d['us_per_matvec_avg']:.2f} us per matvec):\n\n```\n{json.dumps(keep)}\n```\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,7 +481,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the sweeps, copy 256 MiB device->device once, a reference dispatch of known "
                          "size for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-traffic", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "RUN_JSON", "CMD_F", "CMD_W"),
+                    help="write profiles/matvec_qwen3_4b_traffic.{json,md} from two counter runs and exit")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("PROF_DIR", "RUN_JSON", "CMD"),
+                    help="write profiles/matvec_qwen3_4b_kernel_trace.md from a kernel-trace run and exit")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)

@@ -695,33 +695,46 @@ int read_header(const void *header, nwc_header_t &h) {
 
 const uint32_t *item_table(const Geom &g) { return (const uint32_t *)(g.blob + g.off_items); }
 
-// Workgroups a launch keeps resident at once on this device (occupancy
-// query, cached per kernel, block size and LDS), times the compute units; at
-// most 25 waves per compute unit.  Measured on MI355X: the query allows
-// 6 workgroups of 5 waves (30 waves) per CU for the matvec, but grids sized
-// so run slower than ones of 25 waves per CU (some workgroups then start only
-// when others finish).
-int resident_groups(const void *kernel, int block, size_t lds) {
+// Workgroups of a launch one compute unit keeps resident at once (occupancy
+// query, cached per kernel, block size and LDS), at most 25 waves per CU, and
+// the number of CUs.  Measured on MI355X: the query allows 6 workgroups of 5
+// waves (30 waves) per CU for the matvec, but grids sized so run slower than
+// ones of 25 waves per CU.
+struct Residency {
+  int per_cu, cus;
+  size_t lds_per_cu, lds_per_group;  // bytes: one CU's LDS, the most one workgroup may take
+};
+Residency resident_per_cu(const void *kernel, int block, size_t lds) {
   static std::mutex mu;
-  static std::map<std::tuple<int, const void *, int, size_t>, int> cache;
+  static std::map<std::tuple<int, const void *, int, size_t>, Residency> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess) return Residency{0, 0, 0, 0};
   std::lock_guard<std::mutex> lock(mu);
   const auto key = std::make_tuple(dev, kernel, block, lds);
   auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  per_cu = std::min(per_cu, std::max(1, kWavesPerCu / (block / 64)));
-  return cache[key] = per_cu * cus;
+  if (it == cache.end()) {
+    int per_cu = 0, cus = 0, lds_cu = 0, lds_wg = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return Residency{0, 0, 0, 0};
+    per_cu = std::min(per_cu, std::max(1, kWavesPerCu / (block / 64)));
+    it = cache.emplace(key, Residency{per_cu, cus, (size_t)lds_cu, (size_t)lds_wg}).first;
+  }
+  return it->second;
 }
 
-// Persistent grid: as many workgroups as fit at once, each taking the same
-// number of row groups (so no workgroup runs a round more than the others),
-// with at most 8 KiB of row-sum slots per workgroup.  NWC_PERSIST=0 gives one
-// workgroup per row group (for comparisons).
+// Persistent grid: k workgroups on every compute unit, each an equal share
+// (+-1) of consecutive row groups.  A workgroup decodes its groups one after
+// another, so a launch takes about ceil(G / (k * CUs)) group times, and a
+// group time grows with the workgroups sharing a CU (once they are enough to
+// keep it busy); k minimises k * ceil(G / (k * CUs)) over the top quarter of
+// 1..(as many as fit, at most 25 waves), ties to the larger k.  The dynamic LDS request is padded so that no compute unit
+// can take k + 1 workgroups: measured on MI355X, a grid larger than what fits
+// at once leaves some workgroups to start only when others finish, on
+// whichever CU frees first, so CUs end up to 25 % apart.  NWC_PERSIST=0 gives
+// one workgroup per row group (for comparisons).
 struct Launch {
   uint32_t grid, groups_cap;
   size_t lds;
@@ -734,16 +747,29 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel) {
   }();
   const uint32_t slot = g.W * g.R * 4;
   const uint32_t cap_slots = std::max<uint32_t>(1, 8192 / slot);
-  uint32_t grid = n_groups;
-  if (!off) {
-    const int cap = resident_groups(kernel, g.W * 64, matvec_lds(g, std::min<uint32_t>(cap_slots, 4)));
-    if (cap > 0 && (uint32_t)cap < n_groups) {
-      const uint32_t rounds = std::min<uint32_t>((n_groups + cap - 1) / cap, cap_slots);
-      grid = (n_groups + rounds - 1) / rounds;
+  Residency res{0, 0, 0, 0};
+  if (!off) res = resident_per_cu(kernel, g.W * 64, matvec_lds(g, std::min<uint32_t>(cap_slots, 4)));
+  if (res.per_cu <= 0 || n_groups <= (uint32_t)res.cus) return Launch{n_groups, 1, matvec_lds(g, 1)};
+  uint32_t k = 1;
+  uint64_t best = ~0ull;
+  for (uint32_t c = (3 * (uint32_t)res.per_cu + 3) / 4; c <= (uint32_t)res.per_cu; ++c) {
+    const uint64_t grid_c = (uint64_t)c * res.cus;
+    const uint64_t cost = c * ((n_groups + grid_c - 1) / grid_c);
+    if (cost <= best) {
+      best = cost;
+      k = c;
     }
   }
+  uint32_t grid = std::min<uint32_t>(n_groups, k * res.cus);
+  if ((n_groups + grid - 1) / grid > cap_slots) grid = (n_groups + cap_slots - 1) / cap_slots;  // LDS slots bound
   const uint32_t groups_cap = (n_groups + grid - 1) / grid;
-  return Launch{grid, groups_cap, matvec_lds(g, groups_cap)};
+  const size_t need = matvec_lds(g, groups_cap);
+  // One CU's LDS / k in whole KiB less 1 KiB (k workgroups of exactly a k-th did not all fit at once
+  // on MI355X), less the static decode table; at most what a workgroup may take.
+  const size_t per_group = ((res.lds_per_cu / k) & ~(size_t)1023) - 1024;
+  size_t share = per_group > NWC_LUT_BYTES ? per_group - NWC_LUT_BYTES : 0;
+  if (res.lds_per_group > NWC_LUT_BYTES) share = std::min(share, res.lds_per_group - NWC_LUT_BYTES);
+  return Launch{grid, groups_cap, std::max(need, share)};
 }
 
 template <bool FP8, int NG, bool SPLIT>

@@ -25,6 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+CLOCK_HZ = 2.4e9  # MI355X peak engine clock, published
+N_CU = 256
 METRIC = "fused compressed GEMV µs & compressed GB/s (% of HBM peak), Qwen3-4B layer set"
 
 
@@ -128,15 +130,21 @@ def cpu_baseline(S, C):
         gbytes += (enc["coded_bits"] / 8.0 + 2 * k + 4 * n) / 1e9
         weights += n * k
     limit = threadpool_limits(1) if threadpool_limits else None
+    # The sample is decoded and multiplied repeatedly until about 10 s of CPU work have passed.
+    passes = 0
     t0 = time.perf_counter()
-    for enc, x in work:
-        y, A = O.matvec_bf16_ref(O.decode_bf16(enc), x)
+    while passes == 0 or time.perf_counter() - t0 < 10.0:
+        for enc, x in work:
+            y, A = O.matvec_bf16_ref(O.decode_bf16(enc), x)
+        passes += 1
     dt = time.perf_counter() - t0
     if limit is not None and hasattr(limit, "unregister"):
         limit.unregister()
-    return {"value": round(gbytes / dt, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbytes * passes / dt, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)),
             "sample": f"oracle decode + float64 matvec of layer 0's q, k, v, o, gate ({weights / 1e6:.1f} M weights, "
-                      f"host PCG64 draws of the same distributions), single thread, {dt:.1f} s"}
+                      f"host PCG64 draws of the same distributions), single thread (BLAS limited to 1), "
+                      f"{passes} passes, {dt:.1f} s"}
 
 
 def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16, with_fused=False):
@@ -425,6 +433,43 @@ def summarize_traffic(fetch_csv, write_csv, profile_json, cmd_fetch, cmd_write):
     print(json.dumps(d, indent=1))
 
 
+def summarize_counters(csv_path, profile_json, cmd):
+    """One counter run of `--profile-sweeps N` with SQ/GRBM counters -> instructions and clocks per 64 weights."""
+    import collections
+    import csv
+    import statistics
+    meta = json.loads(open(profile_json).read().strip().splitlines()[-1])
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        if "matvec_kernel" in r["Kernel_Name"]:
+            per[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    mean = {c: statistics.mean(v) for c, v in per.items()}
+    w64 = meta["weights_per_matvec"] / 64.0
+    derived = {}
+    if "SQ_INSTS_VALU" in mean:
+        derived["VALU instructions per 64 weights (wave-level)"] = mean["SQ_INSTS_VALU"] / w64
+    if "SQ_INSTS_LDS" in mean:
+        derived["LDS instructions per 64 weights"] = mean["SQ_INSTS_LDS"] / w64
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
+        derived["LDS bank-conflict cycles / LDS active cycles"] = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"]
+    if "GRBM_GUI_ACTIVE" in mean:
+        derived["GRBM_GUI_ACTIVE per matvec"] = mean["GRBM_GUI_ACTIVE"]
+    with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_counters.md"), "w") as f:
+        f.write("# matvec kernel instruction and LDS counters, Qwen3-4B layer set (252 matvecs), MI355X\n\n"
+                "Command (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT`):\n\n"
+                f"    {cmd}\n\nSummarised with `python bench.py --summarize-counters`.\n\n"
+                f"Kernel source hash: {meta['kernel_source_hash']}\n\n"
+                f"Mean per matvec dispatch ({len(next(iter(per.values())))} dispatches, "
+                f"{meta['weights_per_matvec'] / 1e6:.2f} M weights each on average):\n\n"
+                "| counter | mean per dispatch |\n|---|---|\n")
+        for c in sorted(mean):
+            f.write(f"| {c} | {mean[c]:.4g} |\n")
+        f.write("\n| derived | value |\n|---|---|\n")
+        for k, v in derived.items():
+            f.write(f"| {k} | {v:.4g} |\n")
+    print(json.dumps({"mean": mean, "derived": derived}, indent=1))
+
+
 def summarize_trace(prof_dir, bench_json, cmd):
     """Kernel-trace run of the layer set -> per-kernel and per-launch-shape durations."""
     import collections
@@ -485,12 +530,17 @@ def main():
                     help="write profiles/matvec_qwen3_4b_traffic.{json,md} from two counter runs and exit")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("PROF_DIR", "RUN_JSON", "CMD"),
                     help="write profiles/matvec_qwen3_4b_kernel_trace.md from a kernel-trace run and exit")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("CSV", "RUN_JSON", "CMD"),
+                    help="write profiles/matvec_qwen3_4b_counters.md from an SQ/GRBM counter run and exit")
     args = ap.parse_args()
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -534,6 +584,7 @@ def main():
         print(json.dumps({"profile_sweeps": args.profile_sweeps, "matvecs_per_sweep": n_launch,
                           "algo_bytes_per_matvec": sum(m["algo_bytes"] for m in mats) / n_launch,
                           "blob_bytes_per_matvec": sum(m["blob_bytes"] for m in mats) / n_launch,
+                          "weights_per_matvec": sum(m["n"] * m["k"] for m in mats) / n_launch,
                           "copy_calibration_bytes": (64 << 20) * 4 if args.copy_calibration else 0,
                           "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
@@ -580,9 +631,49 @@ def main():
                            "bits_per_weight_blob": round(group[0]["blob_bytes"] * 8 / (n * k), 4),
                            "geometry": {f: group[0]["info"][f] for f in ("cols_per_lane", "rows_per_wave", "waves_per_group", "n_spans")}}
 
+    # Decode clocks per 64 weights: CU-clocks (time x MI355X's 2.4 GHz peak engine
+    # clock x 256 CUs) over weights / 64, for the cold sweep and for one gate
+    # matrix replayed while its 38 MB blob stays in the 256 MB last-level cache
+    # (the decode-bound setting).
+    n_w = sum(m["n"] * m["k"] for m in mats)
+
+    def cu_clocks_per_64w(seconds, weights):
+        return round(seconds * CLOCK_HZ * N_CU / (weights / 64.0), 2)
+
+    gate = next(m for m in mats if m["name"] == "gate")
+    hg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(hg):
+        for _ in range(20):
+            gate["dm"].matvec(gate["x"], gate["y"])
+    hms = time_region(torch, hg.replay, max(3, args.steps // 2), 2) / 20
+    decode_clocks = {"cold_sweep": cu_clocks_per_64w(ms * 1e-3, n_w),
+                     "cache_resident_gate": cu_clocks_per_64w(hms * 1e-3, gate["n"] * gate["k"]),
+                     "cache_resident_gate_us": round(hms * 1e3, 3), "clock_GHz": CLOCK_HZ / 1e9, "cus": N_CU}
+
     # The same layers as a decoder runs them: projections sharing an input fused
     # (q||k||v, gate||up), 4 launches per layer instead of 7.
     fused = measure_fused(torch, fmats, args) if fmats else None
+
+    # Achievable bandwidth for the same launch pattern: one torch.sum per buffer of
+    # each blob's size, same order, graph-replayed (a plain streaming read).
+    stream = None
+    if not args.no_bf16_baseline:
+        bufs = [torch.zeros(m["blob_bytes"] // 2, dtype=torch.bfloat16, device=dev) for m in mats]
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg):
+            for b in bufs:
+                b.sum()
+        sms = time_region(torch, sg.replay, max(3, args.steps // 2), 2)
+        big = torch.zeros(1 << 29, dtype=torch.bfloat16, device=dev)
+        bgr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bgr):
+            big.sum()
+        bigms = time_region(torch, bgr.replay, max(3, args.steps // 2), 2)
+        stream = {"same_launches_GBps": round(blob / (sms * 1e-3) / 1e9, 1),
+                  "one_GiB_GBps": round((1 << 30) / (bigms * 1e-3) / 1e9, 1),
+                  "compressed_blob_GBps_vs_same_launches": round((blob / (ms * 1e-3)) / (blob / (sms * 1e-3)), 4),
+                  "kernel": "torch.sum over bf16 buffers (plain streaming read)"}
+        del bufs, big
 
     bf16 = None
     if not args.no_bf16_baseline:
@@ -628,7 +719,8 @@ def main():
         "effective_bf16_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1),
         "blob_GBps": round(blob / (ms * 1e-3) / 1e9, 1),
         "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(blob / 1e9, 4), "bf16_GB": round(bf16_bytes / 1e9, 4),
-        "per_shape": per_shape, "bf16_baseline": bf16, "roofline": roof, "cpu_baseline": cpu,
+        "per_shape": per_shape, "bf16_baseline": bf16, "stream_read_baseline": stream,
+        "decode_cu_clocks_per_64_weights": decode_clocks, "roofline": roof, "cpu_baseline": cpu,
         "fused_projections": fused,
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -24,7 +24,7 @@ STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPA
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
 EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info",
-           "nwc_workspace_size", "nwc_matvec", "nwc_dequant", "nwc_gather")
+           "nwc_workspace_size", "nwc_matvec", "nwc_dequant", "nwc_gather", "nwc_stream_read")
 
 
 class NWCError(RuntimeError):
@@ -58,6 +58,7 @@ def _load():
         "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
         "nwc_dequant": ([vp, vp, vp, i64, vp], ci),
         "nwc_gather": ([vp, vp, vp, i64, vp, vp], ci),
+        "nwc_stream_read": ([vp, i64, vp, vp], ci),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -144,6 +145,12 @@ def matvec(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -
 
 def dequant(header: np.ndarray, d_blob, out, ld: int, stream=None) -> None:
     _check("nwc_dequant", lib.nwc_dequant(_host_ptr(header), _dev(d_blob), _dev(out), ld, _stream(stream)))
+
+
+def stream_read(buf, sink, nbytes=None, stream=None) -> None:
+    """Plain streaming read of a device tensor (measurement reference); sink: one int32 on the device."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check("nwc_stream_read", lib.nwc_stream_read(_dev(buf), n, _dev(sink), _stream(stream)))
 
 
 def gather(header: np.ndarray, d_blob, ids, out, stream=None) -> None:

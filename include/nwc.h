@@ -135,6 +135,12 @@ int nwc_dequant(const void *header, const void *d_blob, void *d_w, int64_t ld, v
 int nwc_gather(const void *header, const void *d_blob, const int64_t *d_ids, int64_t n_ids,
                void *d_out, void *stream);
 
+/* Measurement helper, not part of the method: a plain streaming read of
+ * `bytes` (a multiple of 16) at d_buf (device, 16-byte aligned) with 16-byte
+ * loads, the achievable-bandwidth reference the matvec is compared with.
+ * d_sink: device, one uint32 the kernel may write (practically never does). */
+int nwc_stream_read(const void *d_buf, int64_t bytes, uint32_t *d_sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

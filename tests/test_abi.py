@@ -228,6 +228,10 @@ def test_launchers_reject_bad_arguments_before_any_gpu_call():
     assert L.nwc_gather(hdr.ctypes.data, fake, fake, -1, fake, None) == -2
     assert L.nwc_gather(hdr.ctypes.data, fake, fake + 4, 5, fake, None) == -1
     assert L.nwc_gather(hdr.ctypes.data, fake, fake, 0, fake, None) == 0   # nothing to do
+    assert L.nwc_stream_read(None, 1024, fake, None) == -1
+    assert L.nwc_stream_read(fake + 8, 1024, fake, None) == -1
+    assert L.nwc_stream_read(fake, 1000, fake, None) == -2
+    assert L.nwc_stream_read(fake, 0, fake, None) == 0   # nothing to read
     q, _ = S.fp8_quantize(S.normal_bf16(3, (200, 700), 0.02))
     h8 = nwc.encode(q, elem=1)[:256].copy()
     assert L.nwc_matvec(h8.ctypes.data, fake, fake, None, fake, None, 0, None) == -1   # fp8 needs a scale

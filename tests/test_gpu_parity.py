@@ -313,3 +313,14 @@ def test_qwen25_step_two_layers_matches_bf16_stack():
     # q||k||v and gate||up encoded as one matrix decode the same weights; only
     # the fp32 summation order of a row may differ.
     assert rel_f < 1e-4
+
+
+def test_stream_read_helper():
+    # The bandwidth reference reads any 16-byte multiple; a zero buffer folds to
+    # zero, so the sink stays untouched.
+    buf = torch.zeros(1 << 20, dtype=torch.int32, device=DEV)
+    sink = torch.full((4,), 7, dtype=torch.int32, device=DEV)
+    for nbytes in (16, 4096 + 16, buf.numel() * 4):
+        nwc.stream_read(buf, sink, nbytes)
+    torch.cuda.synchronize()
+    assert sink.cpu().tolist() == [7, 7, 7, 7]

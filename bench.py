@@ -470,6 +470,56 @@ def summarize_counters(csv_path, profile_json, cmd):
     print(json.dumps({"mean": mean, "derived": derived}, indent=1))
 
 
+def summarize_workload(run_json, cmd):
+    """The JSON line of `--workload qwen25_7b_step` or `--workload tied_embedding` -> its summary under profiles/."""
+    d = json.loads(open(run_json).read().strip().splitlines()[-1])
+    wl = d["config"]["workload"]
+    if wl == "qwen25_7b_decode_step":
+        path = os.path.join(ROOT, "profiles", "qwen25_7b_decode_step.md")
+        b = d.get("bf16_baseline") or {}
+        f_ = d.get("fused_projections") or {}
+        body = ("# Qwen2.5-7B-shaped batch-1 decode step, MI355X\n\n"
+                f"Command (repo root on the GPU box):\n\n    {cmd}\n\n"
+                "28 layers x {q 3584x3584, k/v 512x3584, o 3584x3584, gate/up 18944x3584, down 3584x18944} + lm_head\n"
+                "152064x3584, N(0, 1/sqrt(K)); every linear through `nwc_matvec`; glue in torch (RMS norms with unit\n"
+                "weight, fp32 residual, context-1 attention stand-in = v repeated over the GQA heads, silu(gate)*up).\n"
+                "The same step with `torch.nn.functional.linear` on the BF16 weights is the baseline.\n\n"
+                "| | ms per token | tokens/s |\n|---|---|---|\n"
+                f"| nwc_matvec step, 7 launches per layer (graph replay) | {d['ms_per_step']} | {d['value']} |\n"
+                f"| of which the {d['config']['matrices']} matvecs alone | {d['ms_matvecs_only']} | — |\n")
+        if f_:
+            body += (f"| nwc_matvec step, q\\|\\|k\\|\\|v and gate\\|\\|up fused (4 launches per layer) | "
+                     f"{f_['ms_per_step']} | {f_['tokens_per_s']} |\n")
+        if b:
+            body += f"| BF16 `F.linear` step, same glue | {b['ms_per_step']} | {b['tokens_per_s']} |\n"
+        body += (f"\nMatvecs {d['compressed_GBps_matvecs']} GB/s on {d['compressed_GB']} GB of algorithmic bytes "
+                 f"({d['blob_GB']} GB of blobs)")
+        if b:
+            body += f"; logits relative L2 distance to the BF16 stack {b['logits_rel_l2_vs_bf16_stack']:.2e}"
+        body += f".  Kernel source hash {d['kernel_source_hash']}.\n"
+    elif wl == "tied_embedding":
+        path = os.path.join(ROOT, "profiles", "tied_embedding_and_fp8.md")
+        lm, fp8 = d["lm_head"], d["fp8"]
+        body = ("# Tied embedding / lm_head 151936x2560 and the fp8 e4m3 variant, MI355X\n\n"
+                f"Command (repo root on the GPU box):\n\n    {cmd}\n\n"
+                "| operation | us | rate |\n|---|---|---|\n"
+                f"| lm_head GEMV, nwc_matvec ({lm['blob_MB']} MB blob, > 256 MB last-level cache) | {lm['us']} | "
+                f"{lm['compressed_GBps']} GB/s compressed ({100 * lm['hbm_frac_compressed']:.1f} % of 8 TB/s) |\n"
+                f"| lm_head GEMV, BF16 `F.linear` | {lm['bf16_F_linear_us']} | nwc {lm['speedup_vs_bf16']}x faster |\n"
+                f"| gather of 4096 ids, nwc_gather | {d['gather_4096']['us']} | torch index_select on the BF16 table: "
+                f"{d['gather_4096']['torch_index_select_on_bf16_us']} us |\n"
+                f"| dequantize the whole matrix | {d['dequant_full']['us']} | {d['dequant_full']['GBps_written']} GB/s written |\n")
+        for k, v in fp8.items():
+            body += (f"| fp8 matvec {k} (rotation over {v['rotation']}) | {v['us']} | {v['compressed_GBps']} GB/s, "
+                     f"{v['bits_per_weight_coded']} coded bits/weight |\n")
+        body += ("\nThe 1024x1024 matrices (BF16 and fp8) fit in cache: their times are latency figures, not bandwidth "
+                 f"claims.\nKernel source hash {d['kernel_source_hash']}.\n")
+    else:
+        raise SystemExit(f"no summary for workload {wl}")
+    with open(path, "w") as f:
+        f.write(body + "\n```\n" + json.dumps(d) + "\n```\n")
+
+
 def summarize_trace(prof_dir, bench_json, cmd):
     """Kernel-trace run of the layer set -> per-kernel and per-launch-shape durations."""
     import collections
@@ -530,6 +580,8 @@ def main():
                     help="write profiles/matvec_qwen3_4b_traffic.{json,md} from two counter runs and exit")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("PROF_DIR", "RUN_JSON", "CMD"),
                     help="write profiles/matvec_qwen3_4b_kernel_trace.md from a kernel-trace run and exit")
+    ap.add_argument("--summarize-workload", nargs=2, metavar=("RUN_JSON", "CMD"),
+                    help="write the profiles/ summary of a qwen25_7b_step or tied_embedding run and exit")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("CSV", "RUN_JSON", "CMD"),
                     help="write profiles/matvec_qwen3_4b_counters.md from an SQ/GRBM counter run and exit")
     args = ap.parse_args()
@@ -538,6 +590,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_workload:
+        summarize_workload(*args.summarize_workload)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)

@@ -32,6 +32,7 @@
 //    to finite values, so padding adds exactly zero.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <cstdlib>
 #include <algorithm>
 #include <map>
@@ -187,6 +188,41 @@ __device__ __forceinline__ uint32_t bf16_step(Lane &s) {
   bf16_steps<1>(one, e);
   s = one[0];
   return e[0];
+}
+
+// A lane's stream held in registers: a 128-bit window (four words, least
+// significant first) whose next code starts at bit 2, as the stream's first
+// code does.  Each step shifts the window right by the bits it used, zeros
+// coming in at the top, so the table peek is always bits 2..13 of word 0 and a
+// step needs one LDS access (the table) instead of two.  The window holds an
+// item's whole stream when the item has at most four code rows.
+struct Win {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ void win_shift(Win &s, uint32_t n) {  // n in [0, 31]
+  s.w[0] = __builtin_amdgcn_alignbit(s.w[1], s.w[0], n);
+  s.w[1] = __builtin_amdgcn_alignbit(s.w[2], s.w[1], n);
+  s.w[2] = __builtin_amdgcn_alignbit(s.w[3], s.w[2], n);
+  s.w[3] = s.w[3] >> (n & 31u);
+}
+
+// Next two BF16 codes from the window: a {hiA, hiB, bits} entry.  When a lane
+// of the wave meets an escape or a pair longer than the peek, every lane takes
+// the exact decode; it shifts out code A itself (a pair may use 32 bits) and
+// leaves the bits of code B in the entry for the common shift.
+__device__ __forceinline__ uint32_t bf16_step_win(Win &s, uint32_t lut, uint32_t lo, uint32_t hi) {
+  uint32_t e = lds_load(lut + (s.w[0] & 0x3FFCu));
+  if (__builtin_expect(__any((int)e < 0), 0)) {
+    const uint64_t v = ((((uint64_t)s.w[1]) << 32) | s.w[0]) >> NWC_LEAD_BITS;
+    uint32_t ha, la, hb, lb;
+    bf16_code((uint32_t)v, lo, hi, ha, la);
+    bf16_code((uint32_t)(v >> la), lo, hi, hb, lb);
+    win_shift(s, la);
+    e = ha | (hb << 8) | (lb << 16);
+  }
+  win_shift(s, (e >> 16) & 31u);
+  return e;
 }
 
 
@@ -349,6 +385,26 @@ __device__ __forceinline__ float slice_dot_bf16(Lane &st, const uint4 (&m)[NG], 
   return a0 + a1;
 }
 
+// The same row sum with the lane's stream in a register window.
+template <int NG>
+__device__ __forceinline__ float slice_dot_bf16_win(Win &s, uint32_t lut, uint32_t lo, uint32_t hi,
+                                                    const uint4 (&m)[NG], const X16 (&xv)[NG]) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = bf16_step_win(s, lut, lo, hi);
+      const uint32_t p = __builtin_amdgcn_perm(e, dword_of(m[gi], j >> 1), (j & 1) ? kSelHi : kSelLo);
+      if (j & 1)
+        a1 = dot2(p, xv[gi].v[j], a1);
+      else
+        a0 = dot2(p, xv[gi].v[j], a0);
+    }
+  }
+  return a0 + a1;
+}
+
 template <int NG>
 __device__ __forceinline__ float slice_dot_fp8(Lane &st, const X16 (&xv)[NG]) {
   float a0 = 0.f, a1 = 0.f;
@@ -454,18 +510,21 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   X16 xv[NG];
   load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
-  stage_code(a.code, items, first * a.W + wave, region, lane);
+  uint32_t ahead[PR];
+  fetch_code_ahead<PR>(a.code, items[2 * (first * a.W + wave)], items[2 * (first * a.W + wave) + 1], lane, ahead);
   wait_vm0();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
 
-  uint32_t ahead[PR];
   for (uint32_t grp = first; grp < last; ++grp) {
     const uint32_t item = grp * a.W + wave;
-    if (grp != first) {
-      if (SPLIT) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
-      commit_code_ahead<PR>(a.code, items[2 * item], items[2 * item + 1], region_rows, region, lane, ahead);
-    }
+    // BF16 items of at most four code rows decode from registers; longer ones
+    // (and fp8) from the wave's LDS region.
+    const uint32_t rows = items[2 * item + 1];
+    const bool in_regs = !FP8 && rows <= 4u;
+    if (SPLIT && grp != first) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
+    Win win{{ahead[0], ahead[1], ahead[2], ahead[3]}};
+    if (!in_regs) commit_code_ahead<PR>(a.code, items[2 * item], rows, region_rows, region, lane, ahead);
     // Mantissas of this item, then the next item's code rows: the decode below
     // reads only LDS, so both stream in while it runs (the compiler waits for
     // the mantissas at the multiply-adds, which it places after the decode
@@ -481,8 +540,13 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
       const uint32_t nx = more ? item + a.W : item;
       fetch_code_ahead<PR>(a.code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
     }
-    Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};
-    float v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
+    float v;
+    if (in_regs) {
+      v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
+    } else {
+      Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};
+      v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
+    }
     v = row_sum_lanes(v, S);
     if (row_lane) red[((grp - first) * a.W + wave) * a.R + r] = v;
     if (!SPLIT) {
@@ -685,7 +749,15 @@ size_t matvec_lds(const Geom &g, uint32_t groups_cap) {
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-int launched() { return hipGetLastError() == hipSuccess ? NWC_OK : NWC_ERR_HIP; }
+// Status of the launches just made.  With NWC_DEBUG set, a HIP error is also
+// named on stderr.
+int launched() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return NWC_OK;
+  static const bool debug = getenv("NWC_DEBUG") != nullptr;
+  if (debug) fprintf(stderr, "libnwc: HIP error %d (%s)\n", (int)e, hipGetErrorString(e));
+  return NWC_ERR_HIP;
+}
 
 int read_header(const void *header, nwc_header_t &h) {
   if (!header) return NWC_ERR_ARG;

@@ -46,6 +46,12 @@ class NWCInfo(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libnwc.so not built ({LIB_PATH}); run `python -m decode_matvec_amd.build`")
+    # PyTorch ships its own HIP runtime (soname libamdhip64.so.7, which also
+    # satisfies this library) but asks for it by the unversioned name.  Loaded
+    # first, this library would bind /opt/rocm's runtime and PyTorch would
+    # then load its own beside it: two HIP runtimes in one process, and the
+    # library's finds no device.  Importing torch first leaves one runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     sig = {

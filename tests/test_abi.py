@@ -235,3 +235,17 @@ def test_launchers_reject_bad_arguments_before_any_gpu_call():
     q, _ = S.fp8_quantize(S.normal_bf16(3, (200, 700), 0.02))
     h8 = nwc.encode(q, elem=1)[:256].copy()
     assert L.nwc_matvec(h8.ctypes.data, fake, fake, None, fake, None, 0, None) == -1   # fp8 needs a scale
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # Loading the library before torch once put two HIP runtimes in the process
+    # (PyTorch's bundled one and /opt/rocm's); the library's then saw no device.
+    import subprocess
+    import sys
+    code = ("from decode_matvec_amd import nwc\nimport torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    paths = eval(out.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths

@@ -116,7 +116,7 @@ void build_lut_bf16(const uint8_t *rank_to_sym, uint32_t *lut) {
       if (rb < NWC_ESCAPE_R && (uint32_t)rb + 2 <= avail) {
         const uint32_t lb = rb + 2, sb = (q >> (rb + 1)) & 1;
         const uint32_t ha = (sa << 7) | rank_to_sym[ra], hb = (sb << 7) | rank_to_sym[rb];
-        entry = ha | (hb << 8) | ((la + lb) << 16);
+        entry = (la + lb) | (ha << 8) | (hb << 16);
       }
     }
     lut[p] = entry;

@@ -44,8 +44,8 @@
 namespace {
 
 constexpr int kWavesPerCu = 25;  // persistent grids: waves per compute unit
-constexpr uint32_t kSelLo = 0x05010400u;   // {m[0], hiA, m[1], hiB}
-constexpr uint32_t kSelHi = 0x05030402u;   // {m[2], hiA, m[3], hiB}
+constexpr uint32_t kSelLo = 0x06010500u;   // {m[0], hiA, m[1], hiB}
+constexpr uint32_t kSelHi = 0x06030502u;   // {m[2], hiA, m[3], hiB}
 constexpr uint32_t kSelPair = 0x05040100u; // {a.b0, a.b1, b.b0, b.b1}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -105,7 +105,7 @@ __device__ __forceinline__ uint32_t bf16_pair_exact(uint32_t col_base, uint32_t 
   uint32_t ha, la, hb, lb;
   bf16_code((uint32_t)v, lo, hi, ha, la);
   bf16_code((uint32_t)(v >> la), lo, hi, hb, lb);
-  return ha | (hb << 8) | ((la + lb) << 16);
+  return (la + lb) | (ha << 8) | (hb << 16);
 }
 
 __device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t b) {
@@ -169,7 +169,7 @@ __device__ __forceinline__ void bf16_steps(Lane (&s)[NI], uint32_t (&e)[NI]) {
     for (int i = 0; i < NI; ++i) e[i] = bf16_pair_exact(s[i].col, s[i].Q, s[i].lo, s[i].hi);
   }
 #pragma unroll
-  for (int i = 0; i < NI; ++i) s[i].Q += (e[i] >> 16) & 0xFFu;
+  for (int i = 0; i < NI; ++i) s[i].Q += e[i] & 0xFFu;
 }
 
 // Next fp8 code: returns {bf16 value, byte, bits}.
@@ -190,28 +190,31 @@ __device__ __forceinline__ uint32_t bf16_step(Lane &s) {
   return e[0];
 }
 
-// A lane's stream held in registers: a 128-bit window (four words, least
-// significant first) whose next code starts at bit 2, as the stream's first
-// code does.  Each step shifts the window right by the bits it used, zeros
-// coming in at the top, so the table peek is always bits 2..13 of word 0 and a
-// step needs one LDS access (the table) instead of two.  The window holds an
-// item's whole stream when the item has at most four code rows.
+// A lane's stream held in registers: a window of WN words (least significant
+// first) whose next code starts at bit 2, as the stream's first code does.
+// Each step shifts the window right by the bits it used, zeros coming in at
+// the top, so the table peek is always bits 2..13 of word 0 and a step needs
+// one LDS access (the table) instead of two.  A window of WN words holds the
+// whole stream of an item with at most WN code rows.
+template <int WN>
 struct Win {
-  uint32_t w[4];
+  uint32_t w[WN];
 };
 
-__device__ __forceinline__ void win_shift(Win &s, uint32_t n) {  // n in [0, 31]
-  s.w[0] = __builtin_amdgcn_alignbit(s.w[1], s.w[0], n);
-  s.w[1] = __builtin_amdgcn_alignbit(s.w[2], s.w[1], n);
-  s.w[2] = __builtin_amdgcn_alignbit(s.w[3], s.w[2], n);
-  s.w[3] = s.w[3] >> (n & 31u);
+// Shift right by n mod 32 (the shifts use the low five bits of n).
+template <int WN>
+__device__ __forceinline__ void win_shift(Win<WN> &s, uint32_t n) {
+#pragma unroll
+  for (int i = 0; i + 1 < WN; ++i) s.w[i] = __builtin_amdgcn_alignbit(s.w[i + 1], s.w[i], n);
+  s.w[WN - 1] = s.w[WN - 1] >> (n & 31u);
 }
 
-// Next two BF16 codes from the window: a {hiA, hiB, bits} entry.  When a lane
+// Next two BF16 codes from the window: a {bits, hiA, hiB} entry.  When a lane
 // of the wave meets an escape or a pair longer than the peek, every lane takes
 // the exact decode; it shifts out code A itself (a pair may use 32 bits) and
 // leaves the bits of code B in the entry for the common shift.
-__device__ __forceinline__ uint32_t bf16_step_win(Win &s, uint32_t lut, uint32_t lo, uint32_t hi) {
+template <int WN>
+__device__ __forceinline__ uint32_t bf16_step_win(Win<WN> &s, uint32_t lut, uint32_t lo, uint32_t hi) {
   uint32_t e = lds_load(lut + (s.w[0] & 0x3FFCu));
   if (__builtin_expect(__any((int)e < 0), 0)) {
     const uint64_t v = ((((uint64_t)s.w[1]) << 32) | s.w[0]) >> NWC_LEAD_BITS;
@@ -219,9 +222,9 @@ __device__ __forceinline__ uint32_t bf16_step_win(Win &s, uint32_t lut, uint32_t
     bf16_code((uint32_t)v, lo, hi, ha, la);
     bf16_code((uint32_t)(v >> la), lo, hi, hb, lb);
     win_shift(s, la);
-    e = ha | (hb << 8) | (lb << 16);
+    e = lb | (ha << 8) | (hb << 16);
   }
-  win_shift(s, (e >> 16) & 31u);
+  win_shift(s, e);
   return e;
 }
 
@@ -386,8 +389,8 @@ __device__ __forceinline__ float slice_dot_bf16(Lane &st, const uint4 (&m)[NG], 
 }
 
 // The same row sum with the lane's stream in a register window.
-template <int NG>
-__device__ __forceinline__ float slice_dot_bf16_win(Win &s, uint32_t lut, uint32_t lo, uint32_t hi,
+template <int NG, int WN>
+__device__ __forceinline__ float slice_dot_bf16_win(Win<WN> &s, uint32_t lut, uint32_t lo, uint32_t hi,
                                                     const uint4 (&m)[NG], const X16 (&xv)[NG]) {
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -518,17 +521,17 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
 
   for (uint32_t grp = first; grp < last; ++grp) {
     const uint32_t item = grp * a.W + wave;
-    // BF16 items of at most four code rows decode from registers; longer ones
-    // (and fp8) from the wave's LDS region.
+    // BF16 items of at most four code rows decode from a register window of
+    // two, three or four words; longer ones (and fp8) from the wave's LDS region.
     const uint32_t rows = items[2 * item + 1];
-    const bool in_regs = !FP8 && rows <= 4u;
+    const uint32_t wn = FP8 || rows > 4u ? 0u : rows < 2u ? 2u : rows;
     if (SPLIT && grp != first) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
-    Win win{{ahead[0], ahead[1], ahead[2], ahead[3]}};
-    if (!in_regs) commit_code_ahead<PR>(a.code, items[2 * item], rows, region_rows, region, lane, ahead);
+    const uint32_t cur[4] = {ahead[0], ahead[1], ahead[2], ahead[3]};
+    if (wn == 0) commit_code_ahead<PR>(a.code, items[2 * item], rows, region_rows, region, lane, ahead);
     // Mantissas of this item, then the next item's code rows: the decode below
-    // reads only LDS, so both stream in while it runs (the compiler waits for
+    // needs neither, so both stream in while it runs (the compiler waits for
     // the mantissas at the multiply-adds, which it places after the decode
-    // steps, and for the code rows at the next commit).
+    // steps, and for the code rows where the next item starts).
     uint4 m[NG];
     if (!FP8) {
       const uint4 *mp = (const uint4 *)(a.mant + (uint64_t)item * (64 * C)) + lane;
@@ -541,7 +544,14 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
       fetch_code_ahead<PR>(a.code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
     }
     float v;
-    if (in_regs) {
+    if (wn == 2) {
+      Win<2> win{{cur[0], cur[1]}};
+      v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
+    } else if (wn == 3) {
+      Win<3> win{{cur[0], cur[1], cur[2]}};
+      v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
+    } else if (wn == 4) {
+      Win<4> win{{cur[0], cur[1], cur[2], cur[3]}};
       v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
     } else {
       Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};

@@ -46,7 +46,7 @@
 //
 // Decode table (BF16): entry for peek p (12 stream bits, first bit = bit 0):
 //   two complete codes A, B within the 12 bits:
-//     bits 0..7 high byte of A, 8..15 high byte of B, 16..23 bits used, 31 = 0
+//     bits 0..7 bits used, 8..15 high byte of A, 16..23 high byte of B, 31 = 0
 //   otherwise (escape or a longer pair): bit 31 = 1, rest 0.
 // Decode table (fp8): one code per peek:
 //   bits 0..15 the value as BF16, 16..23 the fp8 byte, 24..30 bits used,
@@ -55,7 +55,7 @@
 #include <stdint.h>
 
 #define NWC_MAGIC 0x3143574Eu /* "NWC1" */
-#define NWC_FORMAT_VERSION 2u
+#define NWC_FORMAT_VERSION 3u
 #define NWC_HEADER_BYTES 256
 #define NWC_LANES 64
 #define NWC_LUT_ENTRIES 4096

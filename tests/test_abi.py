@@ -119,7 +119,7 @@ def test_decode_table_bf16_against_oracle():
             sb, eb, pb = O.parse_one_bf16(pad, pa, r2s)
             ok = pb <= 12 and pb - pa != 16
         if ok:
-            assert e == ((sa << 7) | ea) | (((sb << 7) | eb) << 8) | (pb << 16), p
+            assert e == pb | (((sa << 7) | ea) << 8) | (((sb << 7) | eb) << 16), p
         else:
             assert e == 0x80000000, p
 

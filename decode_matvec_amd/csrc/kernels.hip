@@ -477,8 +477,8 @@ __device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uin
   for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, (int64_t)c0 + 16 * j, k);
 }
 
-// Persistent workgroups: workgroup b decodes the row groups (x column spans)
-// [b*G/grid, (b+1)*G/grid) of the G = n_rowgroups * n_spans in order.  The
+// Persistent workgroups: workgroup b decodes the groups (row group, column
+// span) b, b + grid, b + 2*grid, ... of the G = n_rowgroups * n_spans.  The
 // decode table (and, with one span per row, the activations) is staged once
 // per workgroup.  Each wave fetches the code rows of its next item into
 // registers while it decodes the current one, so after the first item the
@@ -498,8 +498,11 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t first = (uint32_t)((uint64_t)blockIdx.x * a.n_groups / gridDim.x);
-  const uint32_t last = (uint32_t)((uint64_t)(blockIdx.x + 1) * a.n_groups / gridDim.x);
+  // Workgroup b takes groups b, b + grid, b + 2*grid, ...: at any time the
+  // workgroups read neighbouring items, so the machine streams the planes in
+  // order.
+  const uint32_t grid = gridDim.x, first = blockIdx.x;
+  const uint32_t n_mine = (a.n_groups - first + grid - 1) / grid;
   const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
   const uint32_t region_rows = a.region_words >> 6;
   float *red = (float *)(s_dyn + a.W * a.region_words);
@@ -511,6 +514,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
     dma_1k(a.lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
+  const uint32_t step_rg = SPLIT ? grid / a.n_spans : grid, step_sp = grid - step_rg * a.n_spans;
   X16 xv[NG];
   load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
   uint32_t ahead[PR];
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
 
-  for (uint32_t grp = first; grp < last; ++grp) {
+  for (uint32_t i = 0, grp = first; i < n_mine; ++i, grp += grid) {
     const uint32_t item = grp * a.W + wave;
     // BF16 items of at most four code rows decode from a register window of
     // two, three or four words; longer ones (and fp8) from the wave's LDS region.
@@ -539,8 +543,8 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
       for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
     }
     {
-      const bool more = grp + 1 < last;
-      const uint32_t nx = more ? item + a.W : item;
+      const bool more = i + 1 < n_mine;
+      const uint32_t nx = more ? item + grid * a.W : item;
       fetch_code_ahead<PR>(a.code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
     }
     float v;
@@ -558,12 +562,16 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
       v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
     }
     v = row_sum_lanes(v, S);
-    if (row_lane) red[((grp - first) * a.W + wave) * a.R + r] = v;
+    if (row_lane) red[(i * a.W + wave) * a.R + r] = v;
     if (!SPLIT) {
-      ++rg;
-    } else if (++sp == a.n_spans) {
-      sp = 0;
-      ++rg;
+      rg += grid;
+    } else {
+      sp += step_sp;
+      rg += step_rg;
+      if (sp >= a.n_spans) {
+        sp -= a.n_spans;
+        ++rg;
+      }
     }
   }
 
@@ -571,13 +579,13 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   const uint32_t log2R = 6 - a.log2S;
-  const uint32_t n_out = (last - first) << log2R;
+  const uint32_t n_out = n_mine << log2R;
   for (uint32_t t = threadIdx.x; t < n_out; t += blockDim.x) {
     const uint32_t i = t >> log2R, rr = t & (a.R - 1u);
     const float *slot = red + i * a.W * a.R + rr;
     float sum = 0.f;
     for (uint32_t w = 0; w < a.W; ++w) sum += slot[w * a.R];
-    const uint32_t grp = first + i, grow = SPLIT ? grp / a.n_spans : grp;
+    const uint32_t grp = first + i * grid, grow = SPLIT ? grp / a.n_spans : grp;
     store_out<FP8, SPLIT>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial);
   }
 }
@@ -808,7 +816,7 @@ Residency resident_per_cu(const void *kernel, int block, size_t lds) {
 }
 
 // Persistent grid: k workgroups on every compute unit, each an equal share
-// (+-1) of consecutive row groups.  A workgroup decodes its groups one after
+// (+-1) of the row groups, every grid-th one.  A workgroup decodes its groups one after
 // another, so a launch takes about ceil(G / (k * CUs)) group times, and a
 // group time grows with the workgroups sharing a CU (once they are enough to
 // keep it busy); k minimises k * ceil(G / (k * CUs)) over the top quarter of

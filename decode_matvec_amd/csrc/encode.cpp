@@ -177,7 +177,15 @@ struct RowEstimate {
 // times a penalty for workgroups far from 5 waves -- measured on MI355X
 // across the Qwen-shaped matrices: 4-5 waves per workgroup were fastest,
 // 8-10 took 5-20% longer, 2-3 (with padding) longer still.
-double wave_penalty(int W) { return 1.0 + 0.04 * std::max(0, W - 5) + 0.05 * std::max(0, 4 - W); }
+// Relative cost of W waves per workgroup.  The matvec keeps at most 25 waves
+// per compute unit, as floor(25 / W) workgroups of W waves, each with its own
+// copy of the 16 KiB decode table.  Fitted to cold-cache timings on MI355X
+// (Qwen-shaped matrices): time grows as (25 / waves)^0.45 when fewer waves
+// fit, and by about 1.7 % per table copy a compute unit stages.
+double wave_penalty(int W) {
+  const int groups = std::max(1, 25 / W), waves = groups * W;
+  return std::pow(25.0 / waves, 0.45) * (1.0 + 0.017 * groups);
+}
 
 Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req, const RowEstimate &est) {
   std::vector<int> Cs, Rs;
@@ -186,10 +194,9 @@ Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req, const RowEstimate &est)
   if (R_req) Rs = {R_req};
   else Rs = {64, 32, 16, 8, 4, 2, 1};
   // Measured on MI355X (Qwen-shaped matrices, cold cache): 16 columns per lane
-  // is fastest up to ~2^25 weights (more, shorter items pipeline better), 32
-  // above (per-item overheads add up); 48 and 64 only where nothing else fits.
-  const double nk = (double)n * (double)k;
-  auto c_factor = [&](int C) { return C == 16 ? (nk <= (double)(1 << 25) ? 1.0 : 1.15) : C == 32 ? 1.0 : 1.25; };
+  // is fastest (short items decode from a two-word register window and
+  // pipeline better), 32 some 8 % slower; 48 and 64 only where nothing else fits.
+  auto c_factor = [](int C) { return C == 16 ? 1.0 : C == 32 ? 1.08 : 1.25; };
   Geo best;
   double best_cost = 0;
   for (int C : Cs) {

@@ -445,17 +445,14 @@ __device__ __forceinline__ float row_sum_lanes(float a, uint32_t S) {
   return a;
 }
 
-// Geometry of the matrix-vector product, resolved on the host: the plane
-// base pointers instead of the blob and its offsets, and 32-bit sizes (the
-// format caps n and k at 2^31).  All of it is wave-uniform and lives in scalar
-// registers, which also bound how many waves a SIMD takes.  The buffers the
-// kernel reads or writes are __restrict__ kernel arguments of their own: with
-// them the compiler may read the item table through the scalar cache.
+// Geometry of the matrix-vector product resolved on the host, the part a
+// wave does not need at once (the kernel takes the rest as leading scalar
+// arguments): the mantissa plane and 32-bit sizes (the format caps n and k at
+// 2^31).  All of it is wave-uniform and lives in scalar registers, which also
+// bound how many waves a SIMD takes.
 struct MvArgs {
-  const uint8_t *code;  // code plane
   const uint8_t *mant;  // mantissa plane
-  const uint8_t *lut;   // decode table
-  uint32_t n, k, R, W, log2S, n_spans, n_groups, region_words, r2s_lo, r2s_hi, groups_cap;
+  uint32_t n, R, n_spans, region_words, r2s_lo, r2s_hi, groups_cap;
 };
 
 // y[row] (times the fp8 row scale) with one span per row, else the span's
@@ -485,9 +482,19 @@ __device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uin
 // memory system streams while the waves decode.  Row sums go to per-group LDS
 // slots; the outputs are written once every wave is done, each row adding its
 // W wave partials in wave order.
+//
+// What a wave needs first (item table, code plane, decode table, activations,
+// the group count and stride, the item shape) comes as the leading scalar
+// arguments: the build asks for kernel-argument preloading, so gfx950 puts
+// them in scalar registers at wave launch.  Measured on MI355X, a launch's
+// waves otherwise wait up to ~2.5 us for their arguments through the scalar
+// cache.  The buffers are __restrict__, so the compiler may read the item
+// table through the scalar cache.
 template <bool FP8, int NG, bool SPLIT>
-__global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint32_t *__restrict__ items,
-                                                      const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
+                                                      const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
+                                                      uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t k,
+                                                      uint32_t log2S, const MvArgs a,
                                                       const float *__restrict__ scale, float *__restrict__ y,
                                                       float *__restrict__ partial) {
   constexpr uint32_t C = 16 * NG;
@@ -501,37 +508,37 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   // Workgroup b takes groups b, b + grid, b + 2*grid, ...: at any time the
   // workgroups read neighbouring items, so the machine streams the planes in
   // order.
-  const uint32_t grid = gridDim.x, first = blockIdx.x;
-  const uint32_t n_mine = (a.n_groups - first + grid - 1) / grid;
+  const uint32_t first = blockIdx.x;  // grid == gridDim.x
+  const uint32_t n_mine = (n_groups - first + grid - 1) / grid;
   const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
   const uint32_t region_rows = a.region_words >> 6;
-  float *red = (float *)(s_dyn + a.W * a.region_words);
-  const uint32_t S = 1u << a.log2S;
-  const uint32_t r = lane >> a.log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
+  float *red = (float *)(s_dyn + W * a.region_words);
+  const uint32_t S = 1u << log2S;
+  const uint32_t r = lane >> log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
   const bool row_lane = (lane & (S - 1u)) == S - 1u;
 
-  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += a.W)
-    dma_1k(a.lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
+  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += W)
+    dma_1k(lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   const uint32_t step_rg = SPLIT ? grid / a.n_spans : grid, step_sp = grid - step_rg * a.n_spans;
   X16 xv[NG];
-  load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
+  load_x_slice<NG>(x, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
   uint32_t ahead[PR];
-  fetch_code_ahead<PR>(a.code, items[2 * (first * a.W + wave)], items[2 * (first * a.W + wave) + 1], lane, ahead);
+  fetch_code_ahead<PR>(code, items[2 * (first * W + wave)], items[2 * (first * W + wave) + 1], lane, ahead);
   wait_vm0();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
 
   for (uint32_t i = 0, grp = first; i < n_mine; ++i, grp += grid) {
-    const uint32_t item = grp * a.W + wave;
+    const uint32_t item = grp * W + wave;
     // BF16 items of at most four code rows decode from a register window of
     // two, three or four words; longer ones (and fp8) from the wave's LDS region.
     const uint32_t rows = items[2 * item + 1];
     const uint32_t wn = FP8 || rows > 4u ? 0u : rows < 2u ? 2u : rows;
-    if (SPLIT && grp != first) load_x_slice<NG>(x, a.k, xv, ((sp * a.W + wave) << a.log2S) * C + lane_c);
+    if (SPLIT && grp != first) load_x_slice<NG>(x, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
     const uint32_t cur[4] = {ahead[0], ahead[1], ahead[2], ahead[3]};
-    if (wn == 0) commit_code_ahead<PR>(a.code, items[2 * item], rows, region_rows, region, lane, ahead);
+    if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead);
     // Mantissas of this item, then the next item's code rows: the decode below
     // needs neither, so both stream in while it runs (the compiler waits for
     // the mantissas at the multiply-adds, which it places after the decode
@@ -544,8 +551,8 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
     }
     {
       const bool more = i + 1 < n_mine;
-      const uint32_t nx = more ? item + grid * a.W : item;
-      fetch_code_ahead<PR>(a.code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
+      const uint32_t nx = more ? item + grid * W : item;
+      fetch_code_ahead<PR>(code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
     }
     float v;
     if (wn == 2) {
@@ -562,7 +569,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
       v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
     }
     v = row_sum_lanes(v, S);
-    if (row_lane) red[(i * a.W + wave) * a.R + r] = v;
+    if (row_lane) red[(i * W + wave) * a.R + r] = v;
     if (!SPLIT) {
       rg += grid;
     } else {
@@ -578,13 +585,13 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const MvArgs a, const uint
   // Outputs: row (group i, r) = sum over waves w of slot[i][w][r], w ascending.
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
-  const uint32_t log2R = 6 - a.log2S;
+  const uint32_t log2R = 6 - log2S;
   const uint32_t n_out = n_mine << log2R;
   for (uint32_t t = threadIdx.x; t < n_out; t += blockDim.x) {
     const uint32_t i = t >> log2R, rr = t & (a.R - 1u);
-    const float *slot = red + i * a.W * a.R + rr;
+    const float *slot = red + i * W * a.R + rr;
     float sum = 0.f;
-    for (uint32_t w = 0; w < a.W; ++w) sum += slot[w * a.R];
+    for (uint32_t w = 0; w < W; ++w) sum += slot[w * a.R];
     const uint32_t grp = first + i * grid, grow = SPLIT ? grp / a.n_spans : grp;
     store_out<FP8, SPLIT>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial);
   }
@@ -866,22 +873,17 @@ template <bool FP8, int NG, bool SPLIT>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
   const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT>);
   MvArgs a;
-  a.code = g.blob + g.off_code;
   a.mant = g.blob + g.off_mant;
-  a.lut = g.blob + g.off_lut;
   a.n = (uint32_t)g.n;
-  a.k = (uint32_t)g.k;
   a.R = g.R;
-  a.W = g.W;
-  a.log2S = g.log2S;
   a.n_spans = g.n_spans;
-  a.n_groups = g.n_rowgroups * g.n_spans;
   a.region_words = g.region_words;
   a.r2s_lo = g.r2s_lo;
   a.r2s_hi = g.r2s_hi;
   a.groups_cap = L.groups_cap;
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT>), dim3(L.grid), dim3(g.W * 64), L.lds, s, a, item_table(g),
-                     (const uint16_t *)d_x, d_scale, d_y, partial);
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT>), dim3(L.grid), dim3(g.W * 64), L.lds, s, item_table(g),
+                     g.blob + g.off_code, g.blob + g.off_lut, (const uint16_t *)d_x, g.n_rowgroups * g.n_spans, g.W,
+                     L.grid, (uint32_t)g.k, g.log2S, a, d_scale, d_y, partial);
   if (g.n_spans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
                        g.n_spans, g.n, d_scale, d_y);

@@ -351,6 +351,39 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
     print(json.dumps(out_j), flush=True)
 
 
+def measure_batch(torch, mats, args, ms_single, batch=4):
+    """The layer-set sweep with `batch` activation rows per matrix through
+    nwc_matvec_batch (each weight decoded once per row group of up to four
+    activation rows), HIP-graph replayed like the batch-1 sweep."""
+    for m in mats:
+        k, n = m["k"], m["n"]
+        ldx = (k + 7) // 8 * 8
+        xb = torch.zeros((batch, ldx), dtype=torch.int16, device=m["x"].device)
+        for b in range(batch):
+            xb[b, :k] = torch.roll(m["x"], shifts=97 * b)
+        m["xb"] = xb
+        m["yb"] = torch.empty((batch, n), dtype=torch.float32, device=m["x"].device)
+
+    def b_sweep():
+        for m in mats:
+            m["dm"].matvec_batch(m["xb"], m["yb"])
+
+    b_sweep()
+    torch.cuda.synchronize()
+    bg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(bg):
+        b_sweep()
+    bms = time_region(torch, bg.replay, args.steps, args.warmup)
+    algo = sum(m["algo_bytes"] for m in mats)
+    for m in mats:
+        del m["xb"], m["yb"]
+    return {"batch": batch, "ms_per_sweep": round(bms, 4), "us_per_layer": round(bms * 1e3 / args.layers, 2),
+            "us_per_layer_per_token": round(bms * 1e3 / args.layers / batch, 2),
+            "weight_GBps": round(algo / (bms * 1e-3) / 1e9, 1),
+            "speedup_vs_batch1_calls": round(batch * ms_single / bms, 3),
+            "note": "nwc_matvec_batch, 4 activation rows per matrix; weights read and decoded once per sweep"}
+
+
 def measure_fused(torch, fmats, args):
     def f_sweep():
         for m in fmats:
@@ -708,6 +741,8 @@ def main():
     # The same layers as a decoder runs them: projections sharing an input fused
     # (q||k||v, gate||up), 4 launches per layer instead of 7.
     fused = measure_fused(torch, fmats, args) if fmats else None
+    # Four tokens at once: each weight decoded once for four activation rows.
+    batch4 = None if args.no_fused else measure_batch(torch, mats, args, ms)
 
     # Achievable bandwidth for the same launch pattern: a plain streaming read
     # (nwc_stream_read, 16-byte loads) of every blob in sweep order, and of 1 GiB.
@@ -776,7 +811,7 @@ def main():
         "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(blob / 1e9, 4), "bf16_GB": round(bf16_bytes / 1e9, 4),
         "per_shape": per_shape, "bf16_baseline": bf16, "stream_read_baseline": stream,
         "decode_cu_clocks_per_64_weights": decode_clocks, "roofline": roof, "cpu_baseline": cpu,
-        "fused_projections": fused,
+        "fused_projections": fused, "batch4": batch4,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(out), flush=True)

@@ -369,43 +369,45 @@ __device__ __forceinline__ Place place(const Geom &g, uint32_t grp, uint32_t wav
 }
 
 // ----------------------------------------------------------------- matvec
-// Row sum of this lane's slice: NG groups of 16 columns, 8 two-code steps each.
-template <int NG>
-__device__ __forceinline__ float slice_dot_bf16(Lane &st, const uint4 (&m)[NG], const X16 (&xv)[NG]) {
-  float a0 = 0.f, a1 = 0.f;
+// Row sums of this lane's slice against B activation rows: NG groups of 16
+// columns, 8 two-code steps each; every decoded pair of weights is used B
+// times.  Each row's sum is formed in the same order whatever B is.
+template <int NG, int B, class Step>
+__device__ __forceinline__ void slice_dot_bf16_rows(Step step, const uint4 (&m)[NG], const X16 (&xv)[B][NG],
+                                                    float (&v)[B]) {
+  float a0[B], a1[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) a0[b] = a1[b] = 0.f;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t e = bf16_step(st);
+      const uint32_t e = step();
       const uint32_t p = __builtin_amdgcn_perm(e, dword_of(m[gi], j >> 1), (j & 1) ? kSelHi : kSelLo);
-      if (j & 1)
-        a1 = dot2(p, xv[gi].v[j], a1);
-      else
-        a0 = dot2(p, xv[gi].v[j], a0);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        if (j & 1)
+          a1[b] = dot2(p, xv[b][gi].v[j], a1[b]);
+        else
+          a0[b] = dot2(p, xv[b][gi].v[j], a0[b]);
+      }
     }
   }
-  return a0 + a1;
+#pragma unroll
+  for (int b = 0; b < B; ++b) v[b] = a0[b] + a1[b];
 }
 
-// The same row sum with the lane's stream in a register window.
-template <int NG, int WN>
-__device__ __forceinline__ float slice_dot_bf16_win(Win<WN> &s, uint32_t lut, uint32_t lo, uint32_t hi,
-                                                    const uint4 (&m)[NG], const X16 (&xv)[NG]) {
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = bf16_step_win(s, lut, lo, hi);
-      const uint32_t p = __builtin_amdgcn_perm(e, dword_of(m[gi], j >> 1), (j & 1) ? kSelHi : kSelLo);
-      if (j & 1)
-        a1 = dot2(p, xv[gi].v[j], a1);
-      else
-        a0 = dot2(p, xv[gi].v[j], a0);
-    }
-  }
-  return a0 + a1;
+// The lane's stream in the wave's LDS region.
+template <int NG, int B>
+__device__ __forceinline__ void slice_dot_bf16(Lane &st, const uint4 (&m)[NG], const X16 (&xv)[B][NG], float (&v)[B]) {
+  slice_dot_bf16_rows<NG, B>([&] { return bf16_step(st); }, m, xv, v);
+}
+
+// The lane's stream in a register window.
+template <int NG, int B, int WN>
+__device__ __forceinline__ void slice_dot_bf16_win(Win<WN> &s, uint32_t lut, uint32_t lo, uint32_t hi,
+                                                   const uint4 (&m)[NG], const X16 (&xv)[B][NG], float (&v)[B]) {
+  slice_dot_bf16_rows<NG, B>([&] { return bf16_step_win(s, lut, lo, hi); }, m, xv, v);
 }
 
 template <int NG>
@@ -453,6 +455,7 @@ __device__ __forceinline__ float row_sum_lanes(float a, uint32_t S) {
 struct MvArgs {
   const uint8_t *mant;  // mantissa plane
   uint32_t n, R, n_spans, region_words, r2s_lo, r2s_hi, groups_cap;
+  uint32_t ldx, ldy;  // elements between the activation rows / output rows of a batch
 };
 
 // y[row] (times the fp8 row scale) with one span per row, else the span's
@@ -460,18 +463,21 @@ struct MvArgs {
 template <bool FP8, bool SPLIT>
 __device__ __forceinline__ void store_out(const MvArgs &a, uint32_t row, uint32_t span, float v,
                                           const float *__restrict__ scale, float *__restrict__ y,
-                                          float *__restrict__ partial) {
+                                          float *__restrict__ partial, uint32_t b = 0) {
   if (row >= a.n) return;
   if (!SPLIT)
-    y[row] = FP8 ? v * scale[row] : v;
+    y[(uint64_t)b * a.ldy + row] = FP8 ? v * scale[row] : v;
   else
     partial[(uint64_t)row * spans_pad(a.n_spans) + span] = v;
 }
 
-template <int NG>
-__device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uint32_t k, X16 (&xv)[NG], uint32_t c0) {
+template <int NG, int B>
+__device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uint32_t ldx, uint32_t k,
+                                             X16 (&xv)[B][NG], uint32_t c0) {
 #pragma unroll
-  for (int j = 0; j < NG; ++j) xv[j] = load_x16(x, (int64_t)c0 + 16 * j, k);
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < NG; ++j) xv[b][j] = load_x16(x + (uint64_t)b * ldx, (int64_t)c0 + 16 * j, k);
 }
 
 // Persistent workgroups: workgroup b decodes the groups (row group, column
@@ -490,7 +496,7 @@ __device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uin
 // waves otherwise wait up to ~2.5 us for their arguments through the scalar
 // cache.  The buffers are __restrict__, so the compiler may read the item
 // table through the scalar cache.
-template <bool FP8, int NG, bool SPLIT>
+template <bool FP8, int NG, bool SPLIT, int B>
 __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
                                                       const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
                                                       uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t k,
@@ -512,7 +518,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
   const uint32_t n_mine = (n_groups - first + grid - 1) / grid;
   const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
   const uint32_t region_rows = a.region_words >> 6;
-  float *red = (float *)(s_dyn + W * a.region_words);
+  float *red = (float *)(s_dyn + W * a.region_words);  // [group][wave][activation row][R]
   const uint32_t S = 1u << log2S;
   const uint32_t r = lane >> log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
   const bool row_lane = (lane & (S - 1u)) == S - 1u;
@@ -522,8 +528,8 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   const uint32_t step_rg = SPLIT ? grid / a.n_spans : grid, step_sp = grid - step_rg * a.n_spans;
-  X16 xv[NG];
-  load_x_slice<NG>(x, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
+  X16 xv[B][NG];
+  load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
   uint32_t ahead[PR];
   fetch_code_ahead<PR>(code, items[2 * (first * W + wave)], items[2 * (first * W + wave) + 1], lane, ahead);
   wait_vm0();
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
     // two, three or four words; longer ones (and fp8) from the wave's LDS region.
     const uint32_t rows = items[2 * item + 1];
     const uint32_t wn = FP8 || rows > 4u ? 0u : rows < 2u ? 2u : rows;
-    if (SPLIT && grp != first) load_x_slice<NG>(x, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
+    if (SPLIT && grp != first) load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
     const uint32_t cur[4] = {ahead[0], ahead[1], ahead[2], ahead[3]};
     if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead);
     // Mantissas of this item, then the next item's code rows: the decode below
@@ -554,22 +560,28 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
       const uint32_t nx = more ? item + grid * W : item;
       fetch_code_ahead<PR>(code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
     }
-    float v;
+    float v[B];
     if (wn == 2) {
       Win<2> win{{cur[0], cur[1]}};
-      v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
+      slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
     } else if (wn == 3) {
       Win<3> win{{cur[0], cur[1], cur[2]}};
-      v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
+      slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
     } else if (wn == 4) {
       Win<4> win{{cur[0], cur[1], cur[2], cur[3]}};
-      v = slice_dot_bf16_win<NG>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv);
+      slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
     } else {
       Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};
-      v = FP8 ? slice_dot_fp8<NG>(st, xv) : slice_dot_bf16<NG>(st, m, xv);
+      if (FP8)
+        v[0] = slice_dot_fp8<NG>(st, xv[0]);
+      else
+        slice_dot_bf16<NG, B>(st, m, xv, v);
     }
-    v = row_sum_lanes(v, S);
-    if (row_lane) red[(i * W + wave) * a.R + r] = v;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      v[b] = row_sum_lanes(v[b], S);
+      if (row_lane) red[((i * W + wave) * B + b) * a.R + r] = v[b];
+    }
     if (!SPLIT) {
       rg += grid;
     } else {
@@ -582,18 +594,20 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
     }
   }
 
-  // Outputs: row (group i, r) = sum over waves w of slot[i][w][r], w ascending.
+  // Outputs: row (group i, activation row b, r) = sum over waves w of
+  // slot[i][w][b][r], w ascending.
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   const uint32_t log2R = 6 - log2S;
-  const uint32_t n_out = n_mine << log2R;
+  const uint32_t n_out = (n_mine * B) << log2R;
   for (uint32_t t = threadIdx.x; t < n_out; t += blockDim.x) {
-    const uint32_t i = t >> log2R, rr = t & (a.R - 1u);
-    const float *slot = red + i * W * a.R + rr;
+    const uint32_t ib = t >> log2R, rr = t & (a.R - 1u);
+    const uint32_t i = ib / B, b = ib - i * B;
+    const float *slot = red + (i * W * B + b) * a.R + rr;
     float sum = 0.f;
-    for (uint32_t w = 0; w < W; ++w) sum += slot[w * a.R];
+    for (uint32_t w = 0; w < W; ++w) sum += slot[w * B * a.R];
     const uint32_t grp = first + i * grid, grow = SPLIT ? grp / a.n_spans : grp;
-    store_out<FP8, SPLIT>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial);
+    store_out<FP8, SPLIT>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial, b);
   }
 }
 
@@ -766,10 +780,11 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
 }
 
 // Dynamic LDS of a dequant workgroup: W code regions + W*R row sums; of a
-// matvec workgroup: W code regions, then per row group it decodes W*R row sums.
+// matvec workgroup: W code regions, then per row group it decodes W*R row
+// sums for each of the B activation rows.
 size_t group_lds(const Geom &g) { return (size_t)g.W * g.region_words * 4 + (size_t)g.W * g.R * 4; }
-size_t matvec_lds(const Geom &g, uint32_t groups_cap) {
-  return (size_t)g.W * g.region_words * 4 + (size_t)groups_cap * g.W * g.R * 4;
+size_t matvec_lds(const Geom &g, uint32_t groups_cap, uint32_t B = 1) {
+  return (size_t)g.W * g.region_words * 4 + (size_t)groups_cap * g.W * g.R * 4 * B;
 }
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -836,17 +851,17 @@ struct Launch {
   uint32_t grid, groups_cap;
   size_t lds;
 };
-Launch matvec_launch_shape(const Geom &g, const void *kernel) {
+Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1) {
   const uint32_t n_groups = g.n_rowgroups * g.n_spans;
   static const bool off = [] {
     const char *e = getenv("NWC_PERSIST");
     return e && e[0] == '0';
   }();
-  const uint32_t slot = g.W * g.R * 4;
+  const uint32_t slot = g.W * g.R * 4 * B;
   const uint32_t cap_slots = std::max<uint32_t>(1, 8192 / slot);
   Residency res{0, 0, 0, 0};
-  if (!off) res = resident_per_cu(kernel, g.W * 64, matvec_lds(g, std::min<uint32_t>(cap_slots, 4)));
-  if (res.per_cu <= 0 || n_groups <= (uint32_t)res.cus) return Launch{n_groups, 1, matvec_lds(g, 1)};
+  if (!off) res = resident_per_cu(kernel, g.W * 64, matvec_lds(g, std::min<uint32_t>(cap_slots, 4), B));
+  if (res.per_cu <= 0 || n_groups <= (uint32_t)res.cus) return Launch{n_groups, 1, matvec_lds(g, 1, B)};
   uint32_t k = 1;
   uint64_t best = ~0ull;
   for (uint32_t c = (3 * (uint32_t)res.per_cu + 3) / 4; c <= (uint32_t)res.per_cu; ++c) {
@@ -860,7 +875,7 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel) {
   uint32_t grid = std::min<uint32_t>(n_groups, k * res.cus);
   if ((n_groups + grid - 1) / grid > cap_slots) grid = (n_groups + cap_slots - 1) / cap_slots;  // LDS slots bound
   const uint32_t groups_cap = (n_groups + grid - 1) / grid;
-  const size_t need = matvec_lds(g, groups_cap);
+  const size_t need = matvec_lds(g, groups_cap, B);
   // One CU's LDS / k in whole KiB less 1 KiB (k workgroups of exactly a k-th did not all fit at once
   // on MI355X), less the static decode table; at most what a workgroup may take.
   const size_t per_group = ((res.lds_per_cu / k) & ~(size_t)1023) - 1024;
@@ -869,10 +884,15 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel) {
   return Launch{grid, groups_cap, std::max(need, share)};
 }
 
-template <bool FP8, int NG, bool SPLIT>
-void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial) {
-  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT>);
+// B activation rows at once (x rows ldx elements apart, y rows ldy apart);
+// B > 1 only for BF16 blobs whose rows fit one workgroup.
+template <bool FP8, int NG, bool SPLIT, int B = 1>
+void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial,
+                   int64_t ldx = 0, int64_t ldy = 0) {
+  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT, B>, B);
   MvArgs a;
+  a.ldx = (uint32_t)ldx;
+  a.ldy = (uint32_t)ldy;
   a.mant = g.blob + g.off_mant;
   a.n = (uint32_t)g.n;
   a.R = g.R;
@@ -881,7 +901,7 @@ void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d
   a.r2s_lo = g.r2s_lo;
   a.r2s_hi = g.r2s_hi;
   a.groups_cap = L.groups_cap;
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT>), dim3(L.grid), dim3(g.W * 64), L.lds, s, item_table(g),
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT, B>), dim3(L.grid), dim3(g.W * 64), L.lds, s, item_table(g),
                      g.blob + g.off_code, g.blob + g.off_lut, (const uint16_t *)d_x, g.n_rowgroups * g.n_spans, g.W,
                      L.grid, (uint32_t)g.k, g.log2S, a, d_scale, d_y, partial);
   if (g.n_spans > 1)
@@ -907,6 +927,17 @@ void launch_matvec_c(const Geom &g, hipStream_t s, const void *d_x, const float 
     case 48: launch_matvec<FP8, 3, false>(g, s, d_x, d_scale, d_y, partial); break;
     default: launch_matvec<FP8, 4, false>(g, s, d_x, d_scale, d_y, partial); break;
   }
+}
+
+// B = 2 or 4 activation rows of a BF16 blob with one span per row and 16 or
+// 32 columns per lane (wider items would not keep B rows of activations in
+// registers).
+template <int B>
+void launch_matvec_rows(const Geom &g, hipStream_t s, const void *d_x, int64_t ldx, float *d_y, int64_t ldy) {
+  if (g.C == 16)
+    launch_matvec<false, 1, false, B>(g, s, d_x, nullptr, d_y, nullptr, ldx, ldy);
+  else
+    launch_matvec<false, 2, false, B>(g, s, d_x, nullptr, d_y, nullptr, ldx, ldy);
 }
 
 template <bool FP8, int NG>
@@ -991,6 +1022,36 @@ int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const fl
     launch_matvec_c<true>(g, s, d_x, d_scale, d_y, partial);
   else
     launch_matvec_c<false>(g, s, d_x, d_scale, d_y, partial);
+  return launched();
+}
+
+int nwc_matvec_batch(const void *header, const void *d_blob, const void *d_x, int64_t ldx, int64_t batch,
+                     const float *d_scale, float *d_y, int64_t ldy, void *d_ws, int64_t ws_bytes, void *stream) {
+  nwc_header_t h;
+  int st = read_header(header, h);
+  if (st != NWC_OK) return st;
+  if (batch < 0 || ldx < h.k || ldy < h.n || ldx % 8 != 0 || ldx >= ((int64_t)1 << 31) || ldy >= ((int64_t)1 << 31))
+    return NWC_ERR_SHAPE;
+  if (batch == 0) return NWC_OK;
+  const bool fp8 = h.elem == NWC_FP8_E4M3;
+  if (!d_blob || !d_x || !d_y || !aligned(d_blob, 16) || !aligned(d_x, 16) || !aligned(d_y, 4)) return NWC_ERR_ARG;
+  if (fp8 != (d_scale != nullptr) || (d_scale && !aligned(d_scale, 4))) return NWC_ERR_ARG;
+  const uint16_t *x = (const uint16_t *)d_x;
+  if (fp8 || h.n_spans > 1 || h.cols_per_lane > 32) {  // one activation row at a time
+    for (int64_t b = 0; b < batch; ++b)
+      if ((st = nwc_matvec(header, d_blob, x + b * ldx, d_scale, d_y + b * ldy, d_ws, ws_bytes, stream)) != NWC_OK)
+        return st;
+    return NWC_OK;
+  }
+  const Geom g = make_geom(h, d_blob);
+  hipStream_t s = (hipStream_t)stream;
+  int64_t b = 0;
+  for (; batch - b >= 4; b += 4) launch_matvec_rows<4>(g, s, x + b * ldx, ldx, d_y + b * ldy, ldy);
+  if (batch - b >= 2) {
+    launch_matvec_rows<2>(g, s, x + b * ldx, ldx, d_y + b * ldy, ldy);
+    b += 2;
+  }
+  if (b < batch) launch_matvec_c<false>(g, s, x + b * ldx, nullptr, d_y + b * ldy, nullptr);
   return launched();
 }
 

@@ -24,7 +24,7 @@ STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPA
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
 EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info",
-           "nwc_workspace_size", "nwc_matvec", "nwc_dequant", "nwc_gather", "nwc_stream_read")
+           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read")
 
 
 class NWCError(RuntimeError):
@@ -62,6 +62,7 @@ def _load():
         "nwc_blob_info": ([vp, i64, ctypes.POINTER(NWCInfo)], ci),
         "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
         "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
+        "nwc_matvec_batch": ([vp, vp, vp, i64, i64, vp, vp, i64, vp, i64, vp], ci),
         "nwc_dequant": ([vp, vp, vp, i64, vp], ci),
         "nwc_gather": ([vp, vp, vp, i64, vp, vp], ci),
         "nwc_stream_read": ([vp, i64, vp, vp], ci),
@@ -149,6 +150,17 @@ def matvec(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -
                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def matvec_batch(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -> None:
+    """y[b] (fp32 rows) = W x[b] for the rows of x (batch x ldx BF16 patterns) into y (batch x ldy fp32)."""
+    batch = x.shape[0]
+    if y.shape[0] != batch:
+        raise ValueError("x and y need the same number of rows")
+    _check("nwc_matvec_batch", lib.nwc_matvec_batch(_host_ptr(header), _dev(d_blob), _dev(x), x.stride(0), batch,
+                                                    _dev(scale), _dev(y), y.stride(0), _dev(ws),
+                                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                                    _stream(stream)))
+
+
 def dequant(header: np.ndarray, d_blob, out, ld: int, stream=None) -> None:
     _check("nwc_dequant", lib.nwc_dequant(_host_ptr(header), _dev(d_blob), _dev(out), ld, _stream(stream)))
 
@@ -182,6 +194,9 @@ class DeviceMatrix:
 
     def matvec(self, x, y, scale=None, stream=None):
         matvec(self.header, self.d_blob, x, y, self.ws, scale, stream)
+
+    def matvec_batch(self, x, y, scale=None, stream=None):
+        matvec_batch(self.header, self.d_blob, x, y, self.ws, scale, stream)
 
     def dequant(self, out, ld=None, stream=None):
         dequant(self.header, self.d_blob, out, self.k if ld is None else ld, stream)

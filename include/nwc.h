@@ -122,6 +122,22 @@ int nwc_workspace_size(const void *header, int64_t *bytes);
 int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const float *d_scale,
                float *d_y, void *d_ws, int64_t ws_bytes, void *stream);
 
+/* Fused decode + matvec for a small batch of activation rows (the pages'
+ * batch-1 "token path" widened to a few tokens; "Fused kernel" and
+ * "Limitations" describe batch 1 and the prefill route, a batch of several
+ * rows is this library's addition): y_b = W x_b for b < batch.
+ *   d_x      device, batch rows of k BF16 patterns, row b at d_x + b*ldx
+ *            elements; ldx >= k and a multiple of 8 (16-byte aligned rows).
+ *   d_y      device, batch rows of n fp32, row b at d_y + b*ldy; ldy >= n.
+ *   d_scale, d_ws, ws_bytes: as nwc_matvec (rows share the workspace in turn).
+ * BF16 blobs with one span per row and at most 32 columns per lane decode
+ * every weight once per group of up to four rows; other blobs run one row
+ * at a time.  Each row is
+ * summed in the same order as nwc_matvec, so row b equals nwc_matvec on x_b
+ * bit for bit.  batch == 0 does nothing. */
+int nwc_matvec_batch(const void *header, const void *d_blob, const void *d_x, int64_t ldx, int64_t batch,
+                     const float *d_scale, float *d_y, int64_t ldy, void *d_ws, int64_t ws_bytes, void *stream);
+
 /* Dequantization to the stored element type ("How it works": dequantization
  * runs on the same decoder).  BF16 blobs write uint16 BF16 patterns, fp8 blobs
  * write the fp8 bytes (the scale is not applied).  Row i of the matrix goes to

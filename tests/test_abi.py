@@ -223,6 +223,16 @@ def test_launchers_reject_bad_arguments_before_any_gpu_call():
     bad = hdr.copy()
     bad[4] = 9  # version
     assert L.nwc_matvec(bad.ctypes.data, fake, fake, None, fake, fake, ws, None) == -4
+    # nwc_matvec_batch(header, blob, x, ldx, batch, scale, y, ldy, ws, ws_bytes, stream)
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 66000, -1, None, fake, 200, fake, ws, None) == -2
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 65992, 3, None, fake, 200, fake, ws, None) == -2  # ldx < k
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 66004, 3, None, fake, 200, fake, ws, None) == -2  # ldx % 8
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 66000, 3, None, fake, 199, fake, ws, None) == -2  # ldy < n
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, 0, 66000, 3, None, fake, 200, fake, ws, None) == -1
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 66000, 3, None, fake + 2, 200, fake, ws, None) == -1
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 66000, 3, fake, fake, 200, fake, ws, None) == -1
+    assert L.nwc_matvec_batch(bad.ctypes.data, fake, fake, 66000, 3, None, fake, 200, fake, ws, None) == -4
+    assert L.nwc_matvec_batch(hdr.ctypes.data, fake, fake, 66000, 0, None, fake, 200, fake, ws, None) == 0
     assert L.nwc_dequant(hdr.ctypes.data, fake, fake, 65999, None) == -2
     assert L.nwc_dequant(hdr.ctypes.data, fake, fake + 2, 66000, None) == -1
     assert L.nwc_gather(hdr.ctypes.data, fake, fake, -1, fake, None) == -2

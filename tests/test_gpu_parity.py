@@ -226,6 +226,47 @@ def test_fp8_all_bytes_and_odd():
     check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8 odd")
 
 
+# ----------------------------------------------------------------- small batches
+def _batch_case(dm, w, k, batch, seed, scale=None, q=None):
+    """nwc_matvec_batch on `batch` activation rows (padded row pitches): every
+    row equals nwc_matvec on that row bit for bit, nothing past a row's n
+    outputs is written, and the first and last rows meet the oracle's bound."""
+    ldx = (k + 7) // 8 * 8 + 8
+    ldy = dm.n + 3
+    xs = [S.activation_bf16(seed + b, k) for b in range(batch)]
+    xh = np.zeros((batch, ldx), dtype=np.uint16)
+    for b in range(batch):
+        xh[b, :k] = xs[b]
+    y = torch.full((batch, ldy), float("nan"), dtype=torch.float32, device=DEV)
+    dm.matvec_batch(dev16(xh), y, scale=None if scale is None else torch.from_numpy(scale).to(DEV))
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert np.isnan(yh[:, dm.n:]).all(), "wrote past a row's outputs"
+    for b in range(batch):
+        assert np.array_equal(yh[b, :dm.n].astype(np.float64), run_matvec(dm, xs[b], scale)), f"row {b}"
+    for b in sorted({0, batch - 1}):
+        y_ref, A = O.matvec_bf16_ref(w, xs[b]) if q is None else O.matvec_fp8_ref(q, scale, xs[b])
+        check_tol(yh[b, :dm.n].astype(np.float64), y_ref, A, f"batch row {b}")
+
+
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 7])
+def test_matvec_batch(batch):
+    print(f"case batch={batch}", flush=True)
+    w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
+    for cols, rows in ((0, 0), (32, 4), (64, 2)):  # 16 and 32 columns per lane batched, 64 row by row
+        dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows), DEV)
+        _batch_case(dm, w, 1024, batch, 600 + batch)
+
+
+def test_matvec_batch_escapes_split_rows_and_fp8():
+    w = S.inject_rare(S.student_t_bf16(81, (1000, 3001)), 82)  # long items decode from LDS
+    _batch_case(nwc.DeviceMatrix(nwc.encode(w), DEV), w, 3001, 5, 700)
+    w2 = S.normal_bf16(8, (200, 66000), 0.02)  # rows over two workgroups: one row at a time
+    _batch_case(nwc.DeviceMatrix(nwc.encode(w2, cols_per_lane=64, rows_per_wave=1), DEV), w2, 66000, 3, 710)
+    q, sc = S.fp8_quantize(S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"]))
+    _batch_case(nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV), None, 1024, 3, 720, scale=sc, q=q)
+
+
 # ----------------------------------------------------------------- full-size workloads
 def _device_matrix(seed, n, k, sigma):
     wt = S.device_normal_bf16(seed, (n, k), sigma, DEV)

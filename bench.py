@@ -291,14 +291,23 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
     y = torch.empty(n, dtype=torch.float32, device=dev)
     algo = dm.info["coded_bits"] / 8.0 + 2 * k + 4 * n
 
-    def graph_of(fn):
+    def graph_of(fn, reps=1):
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn()
+            for _ in range(reps):
+                fn()
         torch.cuda.synchronize()
         return g
+
+    # Work of a few microseconds is captured `reps` times per graph and the
+    # time divided: one short launch per replay would time the host's graph
+    # launches instead.
+    def per_call_ms(fn, reps, steps=None, warmup=None):
+        steps = args.steps if steps is None else steps
+        warmup = args.warmup if warmup is None else warmup
+        return time_region(torch, graph_of(fn, reps).replay, steps, warmup) / reps
 
     ms_mv = time_region(torch, graph_of(lambda: dm.matvec(x, y)).replay, args.steps, args.warmup)
     xb = x.view(torch.bfloat16).view(1, k)
@@ -307,8 +316,8 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
     ms_bf = time_region(torch, graph_of(lambda: F.linear(xb, wt)).replay, args.steps, args.warmup)
     ids = torch.from_numpy(S.token_ids(C.EMBED["ids_seed"], n, C.N_IDS)).to(dev)
     out = torch.empty((C.N_IDS, k), dtype=torch.int16, device=dev)
-    ms_g = time_region(torch, graph_of(lambda: dm.gather(ids, out)).replay, args.steps, args.warmup)
-    ms_emb = time_region(torch, graph_of(lambda: torch.index_select(wt, 0, ids)).replay, args.steps, args.warmup)
+    ms_g = per_call_ms(lambda: dm.gather(ids, out), 8)
+    ms_emb = per_call_ms(lambda: torch.index_select(wt, 0, ids), 8)
     full = torch.empty((n, k), dtype=torch.int16, device=dev)
     ms_dq = time_region(torch, graph_of(lambda: dm.dequant(full)).replay, max(2, args.steps // 4), 1)
     del full
@@ -328,8 +337,8 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
             scs.append(torch.from_numpy(sc).to(dev))
         xf = torch.from_numpy(S.activation_bf16(C.SINGLE["x_seed"], fk).view(np.int16)).to(dev)
         yf = torch.empty(fn_, dtype=torch.float32, device=dev)
-        msf = time_region(torch, graph_of(lambda: [d.matvec(xf, yf, scale=sc) for d, sc in zip(dms, scs)]).replay,
-                          args.steps, args.warmup) / len(dms)
+        reps = max(1, 32 // len(dms))
+        msf = per_call_ms(lambda: [d.matvec(xf, yf, scale=sc) for d, sc in zip(dms, scs)], reps) / len(dms)
         fa = dms[0].info["coded_bits"] / 8.0 + 2 * fk + 4 * fn_
         fp8[tag] = {"us": round(msf * 1e3, 3), "compressed_GBps": round(fa / (msf * 1e-3) / 1e9, 1),
                     "bits_per_weight_coded": round(dms[0].info["coded_bits"] / (fn_ * fk), 4),

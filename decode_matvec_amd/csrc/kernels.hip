@@ -119,24 +119,18 @@ __device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t b) {
   return (s << 15) | ((E + 120u) << 7) | (M << 4);
 }
 
-// One fp8 code at bit Q+2, in the decode table's entry format (slow path).
-__device__ __forceinline__ uint32_t fp8_exact(uint32_t col_base, uint32_t Q, uint32_t lo, uint32_t hi) {
-  const uint32_t v = (uint32_t)window64(col_base, Q + NWC_LEAD_BITS);
-  const uint32_t r = __builtin_ctz(~v | 0x100u);
-  uint32_t s, E, M, len;
-  if (r < NWC_ESCAPE_R) {
-    s = (v >> (r + 1)) & 1u;
-    M = (v >> (r + 2)) & 7u;
-    E = rank_sym(r, lo, hi) & 15u;
-    len = r + 5;
-  } else {
-    s = (v >> 8) & 1u;
-    E = (v >> 9) & 15u;
-    M = (v >> 13) & 7u;
-    len = 16;
+// Escape table of the fp8 decoder: an escape is 8 ones, then the byte's sign,
+// 4-bit exponent field and 3-bit mantissa raw, so its 8 payload bits (stream
+// bits 8..15 of the code) index a 256-entry table of decode-table entries
+// {BF16 value, byte, 16 bits used}.  Each workgroup writes it into LDS right
+// after the decode table (NWC_FP8_ESC_ENTRIES words); with it every fp8 code
+// decodes from a table, escapes included.
+constexpr uint32_t NWC_FP8_ESC_ENTRIES = 256;
+__device__ __forceinline__ void build_fp8_escapes(uint32_t esc, uint32_t tid, uint32_t threads) {
+  for (uint32_t p = tid; p < NWC_FP8_ESC_ENTRIES; p += threads) {
+    const uint32_t b = ((p & 1u) << 7) | (((p >> 1) & 15u) << 3) | (p >> 5);
+    *(lds_u32 *)(size_t)(esc + 4 * p) = fp8_to_bf16(b) | (b << 16) | (16u << 24);
   }
-  const uint32_t b = (s << 7) | (E << 3) | M;
-  return fp8_to_bf16(b) | (b << 16) | (len << 24);
 }
 
 // Decode state of one stream.
@@ -172,14 +166,16 @@ __device__ __forceinline__ void bf16_steps(Lane (&s)[NI], uint32_t (&e)[NI]) {
   for (int i = 0; i < NI; ++i) s[i].Q += e[i] & 0xFFu;
 }
 
-// Next fp8 code: returns {bf16 value, byte, bits}.
+// Next fp8 code: returns {bf16 value, byte, bits}.  The escape table (after
+// the decode table) answers for the peeks the decode table flags.
 __device__ __forceinline__ uint32_t fp8_step(Lane &s) {
   const uint32_t a = word_addr(s.col, s.Q);
   const uint32_t W = __builtin_amdgcn_alignbit(lds_load(a + 256), lds_load(a), s.Q);
-  uint32_t e = lds_load(s.lut + (W & 0x3FFCu));
-  if (__builtin_expect(__any((int)e < 0), 0)) e = fp8_exact(s.col, s.Q, s.lo, s.hi);
-  s.Q += e >> 24;
-  return e;
+  const uint32_t e = lds_load(s.lut + (W & 0x3FFCu));
+  const uint32_t x = lds_load(s.lut + NWC_LUT_BYTES + ((W >> 8) & 0x3FCu));  // payload = bits 10..17 of W
+  const uint32_t v = (int)e < 0 ? x : e;
+  s.Q += v >> 24;
+  return v;
 }
 
 __device__ __forceinline__ uint32_t bf16_step(Lane &s) {
@@ -316,7 +312,7 @@ __device__ __forceinline__ void wait_code_copies() { asm volatile("s_waitcnt vmc
 // makes every wave's copies visible.
 __device__ __forceinline__ void staged_barrier() {
   wait_all_loads();
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS writes too (the fp8 escape table)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -505,7 +501,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
                                                       float *__restrict__ partial) {
   constexpr uint32_t C = 16 * NG;
   constexpr int PR = 2 * NG + 2;  // code rows fetched ahead (an item's rows and its guard rows, typically)
-  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
+  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   // Dynamic LDS: one code region per wave, then groups_cap slots of W*R row
   // sums (matvec_lds on the host sizes it).
   extern __shared__ uint32_t s_dyn[];
@@ -525,6 +521,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
 
   for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += W)
     dma_1k(lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
+  if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   const uint32_t step_rg = SPLIT ? grid / a.n_spans : grid, step_sp = grid - step_rg * a.n_spans;
@@ -691,13 +688,14 @@ __device__ __forceinline__ void slice_decode(Lane &st, const uint4 *mp, Put put)
 template <bool FP8, int NG>
 __global__ __launch_bounds__(1024) void dequant_kernel(Geom g, const uint32_t *__restrict__ items,
                                                        uint8_t *__restrict__ w, int64_t ld) {
-  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
+  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Place pl = place(g, blockIdx.x, wave, lane);
   const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
   dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
+  if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   stage_code(g.blob + g.off_code, items, pl.item, region, lane);
   staged_barrier();
   Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
@@ -717,12 +715,13 @@ template <bool FP8, int NG>
 __global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__restrict__ items,
                                                       const int64_t *__restrict__ ids, int64_t n_ids,
                                                       uint32_t n_sl, uint8_t *__restrict__ out) {
-  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
+  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t waves = blockDim.x >> 6;
   dma_lut(g, lds_addr(s_lut), wave, waves, lane);
+  if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tok = t / n_sl;
@@ -851,7 +850,7 @@ struct Launch {
   uint32_t grid, groups_cap;
   size_t lds;
 };
-Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1) {
+Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1, size_t static_lds = NWC_LUT_BYTES) {
   const uint32_t n_groups = g.n_rowgroups * g.n_spans;
   static const bool off = [] {
     const char *e = getenv("NWC_PERSIST");
@@ -879,8 +878,8 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1) {
   // One CU's LDS / k in whole KiB less 1 KiB (k workgroups of exactly a k-th did not all fit at once
   // on MI355X), less the static decode table; at most what a workgroup may take.
   const size_t per_group = ((res.lds_per_cu / k) & ~(size_t)1023) - 1024;
-  size_t share = per_group > NWC_LUT_BYTES ? per_group - NWC_LUT_BYTES : 0;
-  if (res.lds_per_group > NWC_LUT_BYTES) share = std::min(share, res.lds_per_group - NWC_LUT_BYTES);
+  size_t share = per_group > static_lds ? per_group - static_lds : 0;
+  if (res.lds_per_group > static_lds) share = std::min(share, res.lds_per_group - static_lds);
   return Launch{grid, groups_cap, std::max(need, share)};
 }
 
@@ -889,7 +888,8 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1) {
 template <bool FP8, int NG, bool SPLIT, int B = 1>
 void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial,
                    int64_t ldx = 0, int64_t ldy = 0) {
-  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT, B>, B);
+  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT, B>, B,
+                                       NWC_LUT_BYTES + (FP8 ? NWC_FP8_ESC_ENTRIES * 4 : 0));
   MvArgs a;
   a.ldx = (uint32_t)ldx;
   a.ldy = (uint32_t)ldy;

@@ -197,12 +197,20 @@ struct Win {
   uint32_t w[WN];
 };
 
-// Shift right by n mod 32 (the shifts use the low five bits of n).
+// Shift right by n mod 32 (the shifts use the low five bits of n; n is a
+// decode-table entry or a code length, whose byte 0 is below 32).  Two words
+// shift as one 64-bit value: one instruction instead of two.
 template <int WN>
 __device__ __forceinline__ void win_shift(Win<WN> &s, uint32_t n) {
+  if constexpr (WN == 2) {
+    const uint64_t v = ((((uint64_t)s.w[1]) << 32) | s.w[0]) >> (n & 63u);
+    s.w[0] = (uint32_t)v;
+    s.w[1] = (uint32_t)(v >> 32);
+  } else {
 #pragma unroll
-  for (int i = 0; i + 1 < WN; ++i) s.w[i] = __builtin_amdgcn_alignbit(s.w[i + 1], s.w[i], n);
-  s.w[WN - 1] = s.w[WN - 1] >> (n & 31u);
+    for (int i = 0; i + 1 < WN; ++i) s.w[i] = __builtin_amdgcn_alignbit(s.w[i + 1], s.w[i], n);
+    s.w[WN - 1] = s.w[WN - 1] >> (n & 31u);
+  }
 }
 
 // Next two BF16 codes from the window: a {bits, hiA, hiB} entry.  When a lane

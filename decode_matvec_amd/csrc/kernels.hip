@@ -845,11 +845,11 @@ Residency resident_per_cu(const void *kernel, int block, size_t lds) {
 }
 
 // Persistent grid: k workgroups on every compute unit, each an equal share
-// (+-1) of the row groups, every grid-th one.  A workgroup decodes its groups one after
-// another, so a launch takes about ceil(G / (k * CUs)) group times, and a
-// group time grows with the workgroups sharing a CU (once they are enough to
-// keep it busy); k minimises k * ceil(G / (k * CUs)) over the top quarter of
-// 1..(as many as fit, at most 25 waves), ties to the larger k.  The dynamic LDS request is padded so that no compute unit
+// (+-1) of the row groups, every grid-th one.  k is as many as fit, up to 25
+// waves per compute unit: measured on MI355X, more waves than that slow every
+// shape down (30 waves: +20 %), and any fewer leave the loads too few to hide
+// HBM latency, even where they would give the CUs an equal number of groups
+// (q 4096 x 2560: 5 workgroups 6.29 us, 4 workgroups 6.59 us).  The dynamic LDS request is padded so that no compute unit
 // can take k + 1 workgroups: measured on MI355X, a grid larger than what fits
 // at once leaves some workgroups to start only when others finish, on
 // whichever CU frees first, so CUs end up to 25 % apart.  NWC_PERSIST=0 gives
@@ -869,16 +869,7 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1, si
   Residency res{0, 0, 0, 0};
   if (!off) res = resident_per_cu(kernel, g.W * 64, matvec_lds(g, std::min<uint32_t>(cap_slots, 4), B));
   if (res.per_cu <= 0 || n_groups <= (uint32_t)res.cus) return Launch{n_groups, 1, matvec_lds(g, 1, B)};
-  uint32_t k = 1;
-  uint64_t best = ~0ull;
-  for (uint32_t c = (3 * (uint32_t)res.per_cu + 3) / 4; c <= (uint32_t)res.per_cu; ++c) {
-    const uint64_t grid_c = (uint64_t)c * res.cus;
-    const uint64_t cost = c * ((n_groups + grid_c - 1) / grid_c);
-    if (cost <= best) {
-      best = cost;
-      k = c;
-    }
-  }
+  const uint32_t k = std::max<uint32_t>(1, (uint32_t)res.per_cu);
   uint32_t grid = std::min<uint32_t>(n_groups, k * res.cus);
   if ((n_groups + grid - 1) / grid > cap_slots) grid = (n_groups + cap_slots - 1) / cap_slots;  // LDS slots bound
   const uint32_t groups_cap = (n_groups + grid - 1) / grid;

@@ -232,6 +232,22 @@ __device__ __forceinline__ uint32_t bf16_step_win(Win<WN> &s, uint32_t lut, uint
   return e;
 }
 
+// Next fp8 code from the window: {bf16 value, byte, bits}.  The escape table
+// answers for the peeks the decode table flags (codes longer than the peek,
+// about 1 % of them); the wave reads it only when one of its lanes needs it.
+// Measured on MI355X (9728 x 2560): the bank conflicts of the table reads
+// bound the fp8 decode, and skipping the unneeded ones is 11 % faster.
+template <int WN>
+__device__ __forceinline__ uint32_t fp8_step_win(Win<WN> &s, uint32_t lut) {
+  const uint32_t e = lds_load(lut + (s.w[0] & 0x3FFCu));
+  uint32_t v = e;
+  if (__any((int)e < 0)) {
+    const uint32_t x = lds_load(lut + NWC_LUT_BYTES + ((s.w[0] >> 8) & 0x3FCu));  // payload = bits 10..17
+    v = (int)e < 0 ? x : e;
+  }
+  win_shift(s, v >> 24);
+  return v;
+}
 
 // ----------------------------------------------------------------- staging
 typedef __attribute__((address_space(3))) void lds_void;
@@ -414,15 +430,15 @@ __device__ __forceinline__ void slice_dot_bf16_win(Win<WN> &s, uint32_t lut, uin
   slice_dot_bf16_rows<NG, B>([&] { return bf16_step_win(s, lut, lo, hi); }, m, xv, v);
 }
 
-template <int NG>
-__device__ __forceinline__ float slice_dot_fp8(Lane &st, const X16 (&xv)[NG]) {
+template <int NG, class Step>
+__device__ __forceinline__ float slice_dot_fp8_codes(Step step, const X16 (&xv)[NG]) {
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t ea = fp8_step(st);
-      const uint32_t eb = fp8_step(st);
+      const uint32_t ea = step();
+      const uint32_t eb = step();
       const uint32_t p = __builtin_amdgcn_perm(eb, ea, kSelPair);
       if (j & 1)
         a1 = dot2(p, xv[gi].v[j], a1);
@@ -431,6 +447,18 @@ __device__ __forceinline__ float slice_dot_fp8(Lane &st, const X16 (&xv)[NG]) {
     }
   }
   return a0 + a1;
+}
+
+// The lane's stream in the wave's LDS region.
+template <int NG>
+__device__ __forceinline__ float slice_dot_fp8(Lane &st, const X16 (&xv)[NG]) {
+  return slice_dot_fp8_codes<NG>([&] { return fp8_step(st); }, xv);
+}
+
+// The lane's stream in a register window.
+template <int NG, int WN>
+__device__ __forceinline__ float slice_dot_fp8_win(Win<WN> &s, uint32_t lut, const X16 (&xv)[NG]) {
+  return slice_dot_fp8_codes<NG>([&] { return fp8_step_win(s, lut); }, xv);
 }
 
 // Partial sums live at [row][column span], each row padded to a multiple of
@@ -508,7 +536,10 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
                                                       const float *__restrict__ scale, float *__restrict__ y,
                                                       float *__restrict__ partial) {
   constexpr uint32_t C = 16 * NG;
-  constexpr int PR = 2 * NG + 2;  // code rows fetched ahead (an item's rows and its guard rows, typically)
+  // Code rows fetched ahead: a BF16 item's rows and its guard rows, typically;
+  // an fp8 item (6.75 bits per weight) takes 4 to 6 rows of 16-column slices.
+  constexpr int PR = FP8 ? 2 * NG + 4 : 2 * NG + 2;
+  constexpr uint32_t kWinMax = FP8 ? 6u : 4u;  // longest item decoded from registers
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   // Dynamic LDS: one code region per wave, then groups_cap slots of W*R row
   // sums (matvec_lds on the host sizes it).
@@ -543,12 +574,15 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
 
   for (uint32_t i = 0, grp = first; i < n_mine; ++i, grp += grid) {
     const uint32_t item = grp * W + wave;
-    // BF16 items of at most four code rows decode from a register window of
-    // two, three or four words; longer ones (and fp8) from the wave's LDS region.
+    // Items of at most kWinMax code rows (BF16: 4, fp8: 6) decode from a
+    // register window of that many words (at least two); longer ones from the
+    // wave's LDS region.
     const uint32_t rows = items[2 * item + 1];
-    const uint32_t wn = FP8 || rows > 4u ? 0u : rows < 2u ? 2u : rows;
+    const uint32_t wn = rows > kWinMax ? 0u : rows < 2u ? 2u : rows;
     if (SPLIT && grp != first) load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
-    const uint32_t cur[4] = {ahead[0], ahead[1], ahead[2], ahead[3]};
+    uint32_t cur[kWinMax];
+#pragma unroll
+    for (uint32_t j = 0; j < kWinMax; ++j) cur[j] = ahead[j];
     if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead);
     // Mantissas of this item, then the next item's code rows: the decode below
     // needs neither, so both stream in while it runs (the compiler waits for
@@ -566,15 +600,27 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
       fetch_code_ahead<PR>(code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
     }
     float v[B];
+    auto run_win = [&](auto &win) {
+      if constexpr (FP8)
+        v[0] = slice_dot_fp8_win<NG>(win, lds_addr(s_lut), xv[0]);
+      else
+        slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
+    };
     if (wn == 2) {
       Win<2> win{{cur[0], cur[1]}};
-      slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
+      run_win(win);
     } else if (wn == 3) {
       Win<3> win{{cur[0], cur[1], cur[2]}};
-      slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
+      run_win(win);
     } else if (wn == 4) {
       Win<4> win{{cur[0], cur[1], cur[2], cur[3]}};
-      slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
+      run_win(win);
+    } else if (FP8 && wn == 5) {
+      Win<5> win{{cur[0], cur[1], cur[2], cur[3], cur[kWinMax > 4 ? 4 : 0]}};
+      run_win(win);
+    } else if (FP8 && wn == 6) {
+      Win<6> win{{cur[0], cur[1], cur[2], cur[3], cur[kWinMax > 4 ? 4 : 0], cur[kWinMax > 5 ? 5 : 0]}};
+      run_win(win);
     } else {
       Lane st{region + 4 * lane, lds_addr(s_lut), 0u, a.r2s_lo, a.r2s_hi};
       if (FP8)

@@ -495,6 +495,42 @@ int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info) {
   return NWC_OK;
 }
 
+int nwc_blob_check(const void *blob, int64_t blob_bytes) {
+  if (!blob) return NWC_ERR_ARG;
+  if (blob_bytes < NWC_HEADER_BYTES) return NWC_ERR_CAPACITY;
+  nwc_header_t h;
+  memcpy(&h, blob, sizeof h);
+  const int st = nwc_check_header(&h);
+  if (st != NWC_OK) return st;
+  if ((uint64_t)blob_bytes < h.total_bytes) return NWC_ERR_CAPACITY;
+  const uint8_t *b = (const uint8_t *)blob;
+  // The rank table orders every symbol once (128 exponent/sign symbols, or
+  // the 16 fp8 exponent fields).
+  const int n_sym = h.elem == NWC_BF16 ? 128 : 16;
+  bool seen[128] = {};
+  for (int r = 0; r < n_sym; ++r) {
+    const int sym = h.rank_to_sym[r];
+    if (sym >= n_sym || seen[sym]) return NWC_ERR_FORMAT;
+    seen[sym] = true;
+  }
+  // The decode table is the one that rank table defines.
+  std::vector<uint32_t> lut(NWC_LUT_ENTRIES);
+  if (h.elem == NWC_BF16)
+    build_lut_bf16(h.rank_to_sym, lut.data());
+  else
+    build_lut_fp8(h.rank_to_sym, lut.data());
+  if (memcmp(lut.data(), b + h.off_lut, NWC_LUT_BYTES) != 0) return NWC_ERR_FORMAT;
+  // Every item's code rows lie inside the code plane, whole 256-byte rows,
+  // at least one and at most max_rows (the kernels size their buffers by it).
+  for (uint64_t i = 0; i < h.n_items; ++i) {
+    uint32_t e[2];
+    memcpy(e, b + h.off_items + 8 * i, 8);
+    const uint64_t off = e[0], rows = e[1];
+    if (rows < 1 || rows > h.max_rows || off % 256 || off + rows * 256 > h.code_bytes) return NWC_ERR_FORMAT;
+  }
+  return NWC_OK;
+}
+
 int nwc_workspace_size(const void *header, int64_t *bytes) {
   if (!header || !bytes) return NWC_ERR_ARG;
   nwc_header_t h;

@@ -23,7 +23,7 @@ HEADER_BYTES = 256
 STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPACITY",
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
-EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info",
+EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info", "nwc_blob_check",
            "nwc_workspace_size", "nwc_matvec", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read")
 
 
@@ -60,6 +60,7 @@ def _load():
         "nwc_encode_bound": ([i64, i64, ci, ci, ci, ctypes.POINTER(i64)], ci),
         "nwc_encode": ([vp, i64, i64, i64, ci, ci, ci, vp, i64, ctypes.POINTER(i64)], ci),
         "nwc_blob_info": ([vp, i64, ctypes.POINTER(NWCInfo)], ci),
+        "nwc_blob_check": ([vp, i64], ci),
         "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
         "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
         "nwc_matvec_batch": ([vp, vp, vp, i64, i64, vp, vp, i64, vp, i64, vp], ci),
@@ -125,6 +126,11 @@ def blob_info(blob: np.ndarray) -> dict:
     d = {f: getattr(info, f) for f, _ in NWCInfo._fields_ if f != "rank_to_sym"}
     d["rank_to_sym"] = list(info.rank_to_sym)
     return d
+
+
+def blob_check(blob: np.ndarray) -> None:
+    """Full host-side validation of a blob (header, rank and decode tables, item table); raises NWCError."""
+    _check("nwc_blob_check", lib.nwc_blob_check(_host_ptr(blob), blob.nbytes))
 
 
 def workspace_size(header: np.ndarray) -> int:

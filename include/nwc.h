@@ -101,6 +101,18 @@ int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, i
  * describe it.  blob_bytes: bytes available at `blob` (>= header bytes). */
 int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info);
 
+/* Full validation of a blob in host memory (blob_bytes available at `blob`),
+ * for blobs read from storage: the header as nwc_blob_info checks it, the
+ * rank table (each symbol once), the decode table (equal to the one the rank
+ * table defines: "How it works", frequency-ranked unary code), and the item
+ * table (every item's code rows inside the code plane, 1..max_rows whole
+ * 256-byte rows).  The device entry points trust the item table, whose
+ * offsets bound their memory accesses: check a blob that did not come from
+ * nwc_encode in this process before uploading it.  Reads only; O(blob
+ * header + tables).  NWC_ERR_CAPACITY if blob_bytes is shorter than the blob,
+ * NWC_ERR_FORMAT for any inconsistency. */
+int nwc_blob_check(const void *blob, int64_t blob_bytes);
+
 /* Device workspace bytes nwc_matvec needs for this blob: 0 unless a row is
  * split over several workgroups (n_spans > 1, only for k > 16*64*C/R), then
  * fp32 partial sums of each row per span.  Its contents need no

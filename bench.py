@@ -276,6 +276,56 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_prefill(args, torch, nwc, S, C, dev):
+    """Prefill (several tokens at once) on the Qwen3-4B layer matrices: each
+    matrix dequantized by nwc_dequant into one reused BF16 buffer, then
+    torch.nn.functional.linear (hipBLASLt), against F.linear on the BF16
+    weights; T = 16, 128, 512 tokens, over a rotation of 4 layers (0.8 GB of
+    BF16 weights, so every call reads its weights from HBM)."""
+    from decode_matvec_amd import prefill as P
+    F = torch.nn.functional
+    layers = args.layers or 4
+    mats, _ = build_layer_set(torch, nwc, S, C, dev, layers, True)
+    scratch = torch.empty(max(m["n"] * m["k"] for m in mats), dtype=torch.int16, device=dev)
+    rows = {}
+    for T in (16, 128, 512):
+        xs = {k: torch.from_numpy(np.stack([S.activation_bf16(7000 + t, k) for t in range(T)]).view(np.int16))
+              .to(dev).view(torch.bfloat16) for k in {m["k"] for m in mats}}
+
+        def nwc_pass():
+            for m in mats:
+                P.prefill(m["dm"], xs[m["k"]], scratch=scratch)
+
+        def bf16_pass():
+            for m in mats:
+                F.linear(xs[m["k"]], m["w_bf16"])
+
+        def dequant_pass():
+            for m in mats:
+                m["dm"].dequant(scratch[: m["n"] * m["k"]].view(m["n"], m["k"]))
+
+        res = {}
+        for tag, fn in (("nwc", nwc_pass), ("bf16", bf16_pass), ("dequant_only", dequant_pass)):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            res[tag] = time_region(torch, g.replay, args.steps, args.warmup) * 1e3 / layers  # us per layer
+        rows[str(T)] = {"us_per_layer_nwc": round(res["nwc"], 2), "us_per_layer_bf16": round(res["bf16"], 2),
+                        "us_per_layer_dequant": round(res["dequant_only"], 2),
+                        "nwc_over_bf16": round(res["nwc"] / res["bf16"], 3)}
+        log(f"[bench] prefill T={T}: {rows[str(T)]}")
+    out = {"metric": "prefill: nwc_dequant + hipBLASLt GEMM vs BF16 GEMM, Qwen3-4B layer matrices",
+           "value": rows["128"]["us_per_layer_nwc"], "unit": "us per layer (T=128)", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(rows["128"]["us_per_layer_nwc"] * layers / 1e3, 4),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1/sqrt(K)) BF16 weights)",
+           "config": {"workload": "prefill", "layers": layers, "tokens": [16, 128, 512]},
+           "per_tokens": rows, "kernel_source_hash": kernel_source_hash()}
+    print(json.dumps(out), flush=True)
+
+
 def bench_tied_embedding(args, torch, nwc, S, C, dev):
     """Tied embedding / lm_head 151936 x 2560 N(0, 0.02): the lm_head GEMV (a
     ~575 MB blob, larger than the 256 MB last-level cache, so each call reads
@@ -513,7 +563,7 @@ def summarize_counters(csv_path, profile_json, cmd):
 
 
 def summarize_workload(run_json, cmd):
-    """The JSON line of `--workload qwen25_7b_step` or `--workload tied_embedding` -> its summary under profiles/."""
+    """The JSON line of `--workload qwen25_7b_step`, `tied_embedding` or `prefill` -> its summary under profiles/."""
     d = json.loads(open(run_json).read().strip().splitlines()[-1])
     wl = d["config"]["workload"]
     if wl == "qwen25_7b_decode_step":
@@ -556,6 +606,17 @@ def summarize_workload(run_json, cmd):
                      f"{v['bits_per_weight_coded']} coded bits/weight |\n")
         body += ("\nThe 1024x1024 matrices (BF16 and fp8) fit in cache: their times are latency figures, not bandwidth "
                  f"claims.\nKernel source hash {d['kernel_source_hash']}.\n")
+    elif wl == "prefill":
+        path = os.path.join(ROOT, "profiles", "prefill_qwen3_4b.md")
+        body = ("# Prefill on the Qwen3-4B layer matrices: nwc_dequant + hipBLASLt GEMM vs the BF16 GEMM, MI355X\n\n"
+                f"Command (repo root on the GPU box):\n\n    {cmd}\n\n"
+                f"{d['config']['layers']} layers x 7 matrices in rotation; every matrix dequantized into one reused BF16 "
+                "buffer, then `torch.nn.functional.linear`; HIP-graph replay.\n\n"
+                "| tokens | nwc us/layer | BF16 us/layer | of which dequant | nwc / BF16 |\n|---|---|---|---|---|\n")
+        for t, r in d["per_tokens"].items():
+            body += (f"| {t} | {r['us_per_layer_nwc']} | {r['us_per_layer_bf16']} | {r['us_per_layer_dequant']} | "
+                     f"{r['nwc_over_bf16']} |\n")
+        body += f"\nKernel source hash {d['kernel_source_hash']}.\n"
     else:
         raise SystemExit(f"no summary for workload {wl}")
     with open(path, "w") as f:
@@ -607,7 +668,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step", "tied_embedding"),
+    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step", "tied_embedding", "prefill"),
                     default="qwen3_4b_layer_set")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -623,7 +684,7 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("PROF_DIR", "RUN_JSON", "CMD"),
                     help="write profiles/matvec_qwen3_4b_kernel_trace.md from a kernel-trace run and exit")
     ap.add_argument("--summarize-workload", nargs=2, metavar=("RUN_JSON", "CMD"),
-                    help="write the profiles/ summary of a qwen25_7b_step or tied_embedding run and exit")
+                    help="write the profiles/ summary of a qwen25_7b_step, tied_embedding or prefill run and exit")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("CSV", "RUN_JSON", "CMD"),
                     help="write profiles/matvec_qwen3_4b_counters.md from an SQ/GRBM counter run and exit")
     args = ap.parse_args()
@@ -656,6 +717,9 @@ def main():
         return
     if args.workload == "tied_embedding":
         bench_tied_embedding(args, torch, nwc, S, C, dev)
+        return
+    if args.workload == "prefill":
+        bench_prefill(args, torch, nwc, S, C, dev)
         return
     args.layers = args.layers or C.QWEN3_4B_LAYERS
     mats, fmats = build_layer_set(torch, nwc, S, C, dev, args.layers,

@@ -267,6 +267,46 @@ def test_matvec_batch_escapes_split_rows_and_fp8():
     _batch_case(nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV), None, 1024, 3, 720, scale=sc, q=q)
 
 
+# ----------------------------------------------------------------- prefill: dequantize + library GEMM
+@pytest.mark.parametrize("tokens", [1, 7, 64])
+def test_prefill_equals_the_library_gemm_on_the_weights(tokens):
+    """Dequantization is exact, so prefill equals F.linear on the original BF16 weights bit for bit (same
+    GEMM, same inputs); fp8 equals the widened e4m3 weights times the row scales.  Both also meet the
+    oracle's bound widened by the GEMM's bf16 output rounding (2^-8 relative)."""
+    import torch.nn.functional as F
+    from decode_matvec_amd import prefill as P
+    print(f"case prefill tokens={tokens}", flush=True)
+    n, k = 1000, 3001
+    w = S.student_t_bf16(91, (n, k))  # finite weights: outputs are compared with torch.equal
+    X = np.stack([S.activation_bf16(900 + t, k) for t in range(tokens)])
+    xt = dev16(X).view(torch.bfloat16)
+    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
+    y = P.prefill(dm, xt)
+    assert y.dtype == torch.bfloat16 and tuple(y.shape) == (tokens, n)
+    assert torch.equal(y, F.linear(xt, dev16(w).view(torch.bfloat16)))
+    yh = y.float().cpu().numpy().astype(np.float64)
+    for t in sorted({0, tokens - 1}):
+        y_ref, A = O.matvec_bf16_ref(w, X[t])
+        assert (np.abs(yh[t] - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + RTOL * A + ATOL).all(), f"token {t}"
+    q, sc = S.fp8_quantize(w)
+    dm8 = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV)
+    scratch = torch.empty(n * k + 100, dtype=torch.uint8, device=DEV)  # larger than needed, reused
+    s_d = torch.from_numpy(sc).to(DEV)
+    wq = torch.from_numpy(q).to(DEV).view(torch.float8_e4m3fn).to(torch.bfloat16)
+    want = (F.linear(xt, wq).float() * s_d[None, :]).to(torch.bfloat16)
+    for _ in range(2):
+        assert torch.equal(P.prefill(dm8, xt, scale=s_d, scratch=scratch), want)
+    y8 = P.prefill(dm8, xt, scale=s_d).float().cpu().numpy().astype(np.float64)
+    y_ref, A = O.matvec_fp8_ref(q, sc, X[0])
+    assert (np.abs(y8[0] - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + RTOL * A + ATOL).all()
+    with pytest.raises(ValueError):
+        P.prefill(dm8, xt)  # fp8 without its scales
+    with pytest.raises(ValueError):
+        P.prefill(dm, xt, scratch=scratch)  # BF16 needs an int16 buffer
+    with pytest.raises(ValueError):
+        P.prefill(dm, xt[:, :100])
+
+
 # ----------------------------------------------------------------- full-size workloads
 def _device_matrix(seed, n, k, sigma):
     wt = S.device_normal_bf16(seed, (n, k), sigma, DEV)

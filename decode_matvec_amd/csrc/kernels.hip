@@ -739,27 +739,132 @@ __device__ __forceinline__ void slice_decode(Lane &st, const uint4 *mp, Put put)
   }
 }
 
+// Decodes NG groups of a lane's slice from a step functor (BF16: one entry
+// per two weights, joined with the mantissa bytes; fp8: one code per step);
+// hands each group of 16 values to put(gi, v).
+template <bool FP8, int NG, class Step, class Put>
+__device__ __forceinline__ void decode_groups(Step step, const uint4 (&m)[NG], Put put) {
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (FP8) {
+        const uint32_t b0 = (step() >> 16) & 0xFFu;
+        const uint32_t b1 = (step() >> 16) & 0xFFu;
+        const uint32_t pair = b0 | (b1 << 8);
+        if (j & 1)
+          v[j >> 1] |= pair << 16;
+        else
+          v[j >> 1] = pair;
+      } else {
+        v[j] = __builtin_amdgcn_perm(step(), dword_of(m[gi], j >> 1), (j & 1) ? kSelHi : kSelLo);
+      }
+    }
+    put(gi, v);
+  }
+}
+
+// Persistent dequantization, on the matvec's scheme: workgroup b decodes the
+// groups b, b + grid, ... with the decode table staged once per workgroup,
+// the next item's code rows fetched into registers while the current item
+// decodes, and items of up to kWinMax code rows decoded from a register
+// window (longer ones from the wave's LDS region).  Each lane stores its
+// 16-column groups straight to the output (16-byte stores when the row pitch
+// allows, element stores for a ragged row end; rows past n store nothing),
+// one item late: at the start of the next item, before its loads.  Stores
+// count with the loads on gfx950, and stores issued after the prefetch made
+// the compiler wait for them, with the prefetch, before every next item.
 template <bool FP8, int NG>
 __global__ __launch_bounds__(1024) void dequant_kernel(Geom g, const uint32_t *__restrict__ items,
                                                        uint8_t *__restrict__ w, int64_t ld) {
+  constexpr int PR = FP8 ? 2 * NG + 4 : 2 * NG + 2;
+  constexpr uint32_t kWinMax = FP8 ? 6u : 4u;
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Place pl = place(g, blockIdx.x, wave, lane);
   const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
-  dma_lut(g, lds_addr(s_lut), wave, g.W, lane);
-  if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
-  stage_code(g.blob + g.off_code, items, pl.item, region, lane);
-  staged_barrier();
-  Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
+  const uint32_t region_rows = g.region_words >> 6;
+  const uint32_t lut = lds_addr(s_lut);
+  const uint8_t *code = g.blob + g.off_code;
+  const uint32_t n_groups = g.n_rowgroups * g.n_spans;
+  const uint32_t first = blockIdx.x, grid = gridDim.x;
+  dma_lut(g, lut, wave, g.W, lane);
+  if (FP8) build_fp8_escapes(lut + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
+  uint32_t ahead[PR];
+  fetch_code_ahead<PR>(code, items[2 * (first * g.W + wave)], items[2 * (first * g.W + wave) + 1], lane, ahead);
+  // Builtin waits (the compiler's wait placement sees them, unlike inline
+  // assembly, so it knows the first item's rows have arrived).
+  wait_vm0();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
   const int64_t esz = FP8 ? 1 : 2;
-  const bool real = pl.row < g.n;
   const bool vec = (ld * esz) % 16 == 0;
-  uint8_t *dst = w + (pl.row * ld + pl.c0) * esz;
-  slice_decode<FP8, NG>(st, FP8 ? nullptr : mant_base(g, pl.item, lane), [&](int gi, const uint32_t(&v)[8]) {
-    if (real) put_group<FP8>(dst + 16 * gi * esz, v, g.k - pl.c0 - 16 * gi, vec);
-  });
+  // The previous item's decoded groups, its output address and columns left.
+  uint32_t out[NG][8];
+  uint8_t *out_dst = w;
+  int64_t out_left = 0;  // <= 0: nothing to store
+  auto flush = [&] {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) put_group<FP8>(out_dst + 16 * gi * esz, out[gi], out_left - 16 * gi, vec);
+  };
+  for (uint32_t grp = first; grp < n_groups; grp += grid) {
+    flush();
+    const Place pl = place(g, grp, wave, lane);
+    const uint32_t rows = items[2 * pl.item + 1];
+    const uint32_t wn = rows > kWinMax ? 0u : rows < 2u ? 2u : rows;
+    uint32_t cur[kWinMax];
+#pragma unroll
+    for (uint32_t j = 0; j < kWinMax; ++j) cur[j] = ahead[j];
+    if (wn == 0) commit_code_ahead<PR>(code, items[2 * pl.item], rows, region_rows, region, lane, ahead);
+    uint4 m[NG];
+    if (!FP8) {
+      const uint4 *mp = mant_base(g, pl.item, lane);
+#pragma unroll
+      for (int j = 0; j < NG; ++j) m[j] = mp[j * 64];
+    }
+    {
+      const bool more = grp + grid < n_groups;
+      const uint32_t nx = more ? (grp + grid) * g.W + wave : pl.item;
+      fetch_code_ahead<PR>(code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
+    }
+    out_dst = w + (pl.row * ld + pl.c0) * esz;
+    out_left = pl.row < g.n ? g.k - pl.c0 : 0;
+    auto put = [&](int gi, const uint32_t(&v)[8]) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[gi][j] = v[j];
+    };
+    auto run_win = [&](auto &win) {
+      if constexpr (FP8)
+        decode_groups<true, NG>([&] { return fp8_step_win(win, lut); }, m, put);
+      else
+        decode_groups<false, NG>([&] { return bf16_step_win(win, lut, g.r2s_lo, g.r2s_hi); }, m, put);
+    };
+    if (wn == 2) {
+      Win<2> win{{cur[0], cur[1]}};
+      run_win(win);
+    } else if (wn == 3) {
+      Win<3> win{{cur[0], cur[1], cur[2]}};
+      run_win(win);
+    } else if (wn == 4) {
+      Win<4> win{{cur[0], cur[1], cur[2], cur[3]}};
+      run_win(win);
+    } else if (FP8 && wn == 5) {
+      Win<5> win{{cur[0], cur[1], cur[2], cur[3], cur[kWinMax > 4 ? 4 : 0]}};
+      run_win(win);
+    } else if (FP8 && wn == 6) {
+      Win<6> win{{cur[0], cur[1], cur[2], cur[3], cur[kWinMax > 4 ? 4 : 0], cur[kWinMax > 5 ? 5 : 0]}};
+      run_win(win);
+    } else {
+      Lane st{region + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
+      if constexpr (FP8)
+        decode_groups<true, NG>([&] { return fp8_step(st); }, m, put);
+      else
+        decode_groups<false, NG>([&] { return bf16_step(st); }, m, put);
+    }
+  }
+  flush();
 }
 
 // Thread t decodes slice t % n_sl of row ids[t / n_sl] (n_sl = ceil(k / C)):
@@ -835,7 +940,6 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
 // Dynamic LDS of a dequant workgroup: W code regions + W*R row sums; of a
 // matvec workgroup: W code regions, then per row group it decodes W*R row
 // sums for each of the B activation rows.
-size_t group_lds(const Geom &g) { return (size_t)g.W * g.region_words * 4 + (size_t)g.W * g.R * 4; }
 size_t matvec_lds(const Geom &g, uint32_t groups_cap, uint32_t B = 1) {
   return (size_t)g.W * g.region_words * 4 + (size_t)groups_cap * g.W * g.R * 4 * B;
 }
@@ -985,10 +1089,28 @@ void launch_matvec_rows(const Geom &g, hipStream_t s, const void *d_x, int64_t l
     launch_matvec<false, 2, false, B>(g, s, d_x, nullptr, d_y, nullptr, ldx, ldy);
 }
 
+// Persistent grid as for the matvec (k workgroups per CU, up to 25 waves, the
+// LDS request padded so that no CU takes k + 1); a workgroup's LDS is its
+// waves' code regions only.
 template <bool FP8, int NG>
 void launch_dequant(const Geom &g, hipStream_t s, void *d_w, int64_t ld) {
-  hipLaunchKernelGGL((dequant_kernel<FP8, NG>), dim3(g.n_rowgroups * g.n_spans), dim3(g.W * 64), group_lds(g), s, g,
-                     item_table(g), (uint8_t *)d_w, ld);
+  const void *kernel = (const void *)dequant_kernel<FP8, NG>;
+  const uint32_t n_groups = g.n_rowgroups * g.n_spans;
+  const size_t regions = (size_t)g.W * g.region_words * 4;
+  const size_t static_lds = NWC_LUT_BYTES + (FP8 ? NWC_FP8_ESC_ENTRIES * 4 : 0);
+  const Residency res = resident_per_cu(kernel, g.W * 64, regions);
+  uint32_t grid = n_groups;
+  size_t lds = regions;
+  if (res.per_cu > 0 && n_groups > (uint32_t)res.cus) {
+    const uint32_t k = (uint32_t)res.per_cu;
+    grid = std::min<uint32_t>(n_groups, k * res.cus);
+    const size_t per_group = ((res.lds_per_cu / k) & ~(size_t)1023) - 1024;
+    size_t share = per_group > static_lds ? per_group - static_lds : 0;
+    if (res.lds_per_group > static_lds) share = std::min(share, res.lds_per_group - static_lds);
+    lds = std::max(lds, share);
+  }
+  hipLaunchKernelGGL((dequant_kernel<FP8, NG>), dim3(grid), dim3(g.W * 64), lds, s, g, item_table(g), (uint8_t *)d_w,
+                     ld);
 }
 
 template <bool FP8>

@@ -272,17 +272,6 @@ __device__ __forceinline__ void dma_lut(const Geom &g, uint32_t lut, uint32_t wa
 
 __device__ __forceinline__ void lds_store(uint32_t byte_addr, uint32_t v) { *(lds_u32 *)(size_t)byte_addr = v; }
 
-// Copies item `item`'s code rows into the wave's LDS region (byte address
-// `region`) and zeroes the two guard rows after them (this lane's column
-// only; the lane is the only reader of its column).
-__device__ __forceinline__ void stage_code(const uint8_t *code, const uint32_t *__restrict__ items, uint32_t item,
-                                           uint32_t region, uint32_t lane) {
-  const uint32_t off = items[2 * item], rows = items[2 * item + 1];
-  dma_to_lds(code + off, region, rows * 256, lane);
-  lds_store(region + rows * 256 + 4 * lane, 0u);
-  lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
-}
-
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // The same waits as builtins, which the compiler's own wait placement takes
 // into account (it does not read inline assembly): vmcnt(0), lgkmcnt(0).
@@ -327,10 +316,6 @@ __device__ __forceinline__ void commit_code_ahead(const uint8_t *code, uint32_t 
     wait_vm0();
   }
 }
-// Waits until at most N vector memory operations of this wave are in flight:
-// the last N issued (mantissa chunks) may still be on their way.
-template <int N>
-__device__ __forceinline__ void wait_code_copies() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // Waits for this wave's loads (its LDS copies included), then a bare barrier
 // makes every wave's copies visible.

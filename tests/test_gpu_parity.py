@@ -181,6 +181,49 @@ def test_all_patterns_dequant_and_gather():
     assert np.array_equal(host16(out), O.gather_bf16_ref(enc, ids))
 
 
+def _gather_case(dm, expect_rows, ids, k, elem_u8=False):
+    """nwc_gather of `ids`: each output row equals the expected row bit for bit (ids outside [0, n): zeros)."""
+    dt = torch.uint8 if elem_u8 else torch.int16
+    out = torch.full((len(ids), k), -1, dtype=dt, device=DEV)
+    dm.gather(torch.from_numpy(ids).to(DEV), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    got = got if elem_u8 else got.view(np.uint16)
+    assert np.array_equal(got, expect_rows), f"gather differs in rows {np.nonzero((got != expect_rows).any(1))[0][:8]}"
+
+
+def _ids_for(n, seed, count=300):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, n, count).astype(np.int64)
+    ids[:6] = [0, n - 1, -1, n, 1 << 40, ids[6]]  # ends, out of range on both sides, a duplicate
+    return ids
+
+
+@pytest.mark.parametrize("cols,rows", GEOMETRIES)
+def test_gather_every_geometry(cols, rows):
+    """Every work-item geometry, BF16 against the oracle's gather and fp8 against its definition."""
+    print(f"case gather cols={cols} rows={rows}", flush=True)
+    w = S.inject_rare(S.student_t_bf16(31, (1000, 1024)), 32)
+    ids = _ids_for(1000, 33)
+    dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows), DEV)
+    _gather_case(dm, O.gather_bf16_ref(O.encode_bf16(w), ids), ids, 1024)
+    q, _ = S.fp8_quantize(w)
+    dm8 = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_lane=cols, rows_per_wave=rows), DEV)
+    valid = (ids >= 0) & (ids < 1000)
+    _gather_case(dm8, np.where(valid[:, None], q[np.clip(ids, 0, 999)], 0).astype(np.uint8), ids, 1024, True)
+
+
+def test_gather_odd_shapes_and_split_rows():
+    """Ragged K (last 16-column group partial), one-column rows, a row over two workgroups, one id."""
+    for idx, (n, k, cols, rows) in enumerate(((7, 513, 0, 0), (1000, 3001, 0, 0), (4097, 1, 0, 0),
+                                               (3, 65536, 0, 0), (200, 66000, 64, 1), (33, 257, 32, 32))):
+        print(f"case gather shape={(n, k)}", flush=True)
+        w = S.inject_rare(S.student_t_bf16(40 + idx, (n, k)), 50 + idx)
+        dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows), DEV)
+        for ids in (_ids_for(n, 60 + idx, 97), np.array([n // 2], dtype=np.int64)):
+            _gather_case(dm, O.gather_bf16_ref(O.encode_bf16(w), ids), ids, k)
+
+
 # ----------------------------------------------------------------- exact special cases
 def test_exact_special_cases():
     w = S.normal_bf16(31, (200, 300), 0.02)

@@ -507,7 +507,7 @@ def summarize_traffic(fetch_csv, write_csv, profile_json, cmd_fetch, cmd_write):
     json.dump(d, open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.json"), "w"), indent=1)
     with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.md"), "w") as f:
         f.write("# matvec kernel HBM traffic, Qwen3-4B layer set (252 matvecs), MI355X\n\n"
-                "Commands (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT`):\n\n"
+                "Commands (from the repository root on an MI355X machine, with `TMPDIR=/tmp`):\n\n"
                 f"    {cmd_fetch}\n    {cmd_write}\n\nSummarised with `python bench.py --summarize-traffic` "
                 "(the counter CSVs and the JSON line the profiled run printed).\n\n"
                 f"Kernel source hash: {meta['kernel_source_hash']}\n\n"
@@ -548,7 +548,7 @@ def summarize_counters(csv_path, profile_json, cmd):
         derived["GRBM_GUI_ACTIVE per matvec"] = mean["GRBM_GUI_ACTIVE"]
     with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_counters.md"), "w") as f:
         f.write("# matvec kernel instruction and LDS counters, Qwen3-4B layer set (252 matvecs), MI355X\n\n"
-                "Command (repo root on the GPU box, after `cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT`):\n\n"
+                "Command (from the repository root on an MI355X machine, with `TMPDIR=/tmp`):\n\n"
                 f"    {cmd}\n\nSummarised with `python bench.py --summarize-counters`.\n\n"
                 f"Kernel source hash: {meta['kernel_source_hash']}\n\n"
                 f"Mean per matvec dispatch ({len(next(iter(per.values())))} dispatches, "
@@ -571,7 +571,7 @@ def summarize_workload(run_json, cmd):
         b = d.get("bf16_baseline") or {}
         f_ = d.get("fused_projections") or {}
         body = ("# Qwen2.5-7B-shaped batch-1 decode step, MI355X\n\n"
-                f"Command (repo root on the GPU box):\n\n    {cmd}\n\n"
+                f"Command (from the repository root on an MI355X machine):\n\n    {cmd}\n\n"
                 "28 layers x {q 3584x3584, k/v 512x3584, o 3584x3584, gate/up 18944x3584, down 3584x18944} + lm_head\n"
                 "152064x3584, N(0, 1/sqrt(K)); every linear through `nwc_matvec`; glue in torch (RMS norms with unit\n"
                 "weight, fp32 residual, context-1 attention stand-in = v repeated over the GQA heads, silu(gate)*up).\n"
@@ -593,7 +593,7 @@ def summarize_workload(run_json, cmd):
         path = os.path.join(ROOT, "profiles", "tied_embedding_and_fp8.md")
         lm, fp8 = d["lm_head"], d["fp8"]
         body = ("# Tied embedding / lm_head 151936x2560 and the fp8 e4m3 variant, MI355X\n\n"
-                f"Command (repo root on the GPU box):\n\n    {cmd}\n\n"
+                f"Command (from the repository root on an MI355X machine):\n\n    {cmd}\n\n"
                 "| operation | us | rate |\n|---|---|---|\n"
                 f"| lm_head GEMV, nwc_matvec ({lm['blob_MB']} MB blob, > 256 MB last-level cache) | {lm['us']} | "
                 f"{lm['compressed_GBps']} GB/s compressed ({100 * lm['hbm_frac_compressed']:.1f} % of 8 TB/s) |\n"
@@ -609,7 +609,7 @@ def summarize_workload(run_json, cmd):
     elif wl == "prefill":
         path = os.path.join(ROOT, "profiles", "prefill_qwen3_4b.md")
         body = ("# Prefill on the Qwen3-4B layer matrices: nwc_dequant + hipBLASLt GEMM vs the BF16 GEMM, MI355X\n\n"
-                f"Command (repo root on the GPU box):\n\n    {cmd}\n\n"
+                f"Command (from the repository root on an MI355X machine):\n\n    {cmd}\n\n"
                 f"{d['config']['layers']} layers x 7 matrices in rotation; every matrix dequantized into one reused BF16 "
                 "buffer, then `torch.nn.functional.linear`; HIP-graph replay.\n\n"
                 "| tokens | nwc us/layer | BF16 us/layer | of which dequant | nwc / BF16 |\n|---|---|---|---|---|\n")
@@ -640,7 +640,7 @@ def summarize_trace(prof_dir, bench_json, cmd):
     mv = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if "matvec_kernel" in r["Kernel_Name"]]
     with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_kernel_trace.md"), "w") as f:
         f.write("# matvec kernel trace -- Qwen3-4B layer set (36 layers x 7 matrices), MI355X\n\n"
-                "Command (repo root on the GPU box):\n\n    cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT\n"
+                "Command (from the repository root on an MI355X machine, with `TMPDIR=/tmp`):\n\n"
                 f"    {cmd}\n\nSummarised with `python bench.py --summarize-trace`.\n\n"
                 f"Kernel source hash: {d['kernel_source_hash']}\n\n"
                 "`run_kernel_stats.csv`, matvec rows (copy and `at::native` kernels are input set-up outside "

@@ -9,9 +9,11 @@
 static inline int64_t nwc_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline int64_t nwc_round_up(int64_t a, int64_t b) { return nwc_ceil_div(a, b) * b; }
 
-// Decoder LDS of one matvec workgroup: two staged code regions per wave
-// (with guard rows; one decodes while the next fills), two sets of cross-wave
-// row sums, the static decode table.
+// The format's bound on a workgroup's decoder LDS, used by the encoder to
+// choose geometries and by the header check: two code regions per wave (with
+// guard rows), two sets of cross-wave row sums and the static decode table.
+// It is conservative: the kernels use one code region per wave plus their row
+// sums, the decode table and, for fp8, the 1 KiB escape table.
 static inline int64_t nwc_lds_bytes_for(int64_t waves, int64_t rows_per_wave, int64_t max_rows) {
   return 2 * (waves * (max_rows + NWC_GUARD_ROWS) * 256 + waves * rows_per_wave * 4) + NWC_LUT_BYTES;
 }

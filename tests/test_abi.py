@@ -30,6 +30,21 @@ def test_exports_every_declared_symbol():
     assert "format" in nwc.status_string(-4)
 
 
+def test_header_is_plain_c(tmp_path):
+    """include/nwc.h is a C ABI: it compiles as strict C99 and as C++17, without warnings."""
+    import shutil
+    import subprocess
+    src = tmp_path / "use.c"
+    src.write_text('#include "nwc.h"\nint main(void) { nwc_info i; (void)i; return nwc_version() > 0 ? 0 : 1; }\n')
+    inc = os.path.join(ROOT, "include")
+    for cc, args in (("gcc", ["-std=c99", "-pedantic"]), ("g++", ["-std=c++17", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not installed")
+        r = subprocess.run([cc, *args, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc, str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
 def _mats():
     out = [("single", S.normal_bf16(1, (1024, 1024), 0.02)),
            ("all_patterns", S.all_patterns_bf16())]

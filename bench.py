@@ -857,6 +857,26 @@ def main():
                 "speedup_compressed_vs_bf16": round(bms / ms, 4),
                 "kernel": "torch.nn.functional.linear (hipBLASLt/rocBLAS), same rotation"}
 
+        # The library's plain BF16 GEMV (no decode), same weights and rotation: the uncompressed
+        # reference on the same skeleton of 16-byte streaming loads.
+        ys = [torch.empty(m["n"], dtype=torch.float32, device=dev) for m in mats]
+
+        def plain_sweep():
+            for m, yy in zip(mats, ys):
+                nwc.bf16_gemv(m["w_bf16"], m["x_bf16"], yy)
+
+        plain_sweep()
+        torch.cuda.synchronize()
+        pg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pg):
+            plain_sweep()
+        pms = time_region(torch, pg.replay, args.steps, args.warmup)
+        bf16["plain_gemv"] = {"ms_per_sweep": round(pms, 4),
+                              "GBps": round((bf16_bytes + sum(2.0 * (m["n"] + m["k"]) for m in mats)) / (pms * 1e-3) / 1e9, 1),
+                              "speedup_compressed_vs_plain": round(pms / ms, 4),
+                              "kernel": "nwc_bf16_gemv: plain BF16 GEMV, 16-byte streaming loads, no decode"}
+        del ys
+
     algo_per_launch = algo / n_launch
     achieved = algo_per_launch / (ms * 1e-3 / n_launch) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -24,7 +24,8 @@ STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPA
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
 EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info", "nwc_blob_check",
-           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read")
+           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
+           "nwc_bf16_gemv")
 
 
 class NWCError(RuntimeError):
@@ -67,6 +68,7 @@ def _load():
         "nwc_dequant": ([vp, vp, vp, i64, vp], ci),
         "nwc_gather": ([vp, vp, vp, i64, vp, vp], ci),
         "nwc_stream_read": ([vp, i64, vp, vp], ci),
+        "nwc_bf16_gemv": ([vp, i64, i64, i64, vp, vp, vp], ci),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -175,6 +177,15 @@ def stream_read(buf, sink, nbytes=None, stream=None) -> None:
     """Plain streaming read of a device tensor (measurement reference); sink: one int32 on the device."""
     n = buf.numel() * buf.element_size() if nbytes is None else nbytes
     _check("nwc_stream_read", lib.nwc_stream_read(_dev(buf), n, _dev(sink), _stream(stream)))
+
+
+def bf16_gemv(w, x, y, stream=None) -> None:
+    """Plain BF16 GEMV y = W x (the uncompressed measurement baseline): w int16/bfloat16 [n, ldw] device,
+    x [k] device, y fp32 [n] device."""
+    n, ldw = w.shape
+    k = x.numel()
+    _check("nwc_bf16_gemv", lib.nwc_bf16_gemv(_dev(w), n, k, w.stride(0) if w.dim() == 2 else ldw, _dev(x), _dev(y),
+                                              _stream(stream)))
 
 
 def gather(header: np.ndarray, d_blob, ids, out, stream=None) -> None:

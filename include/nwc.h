@@ -169,6 +169,15 @@ int nwc_gather(const void *header, const void *d_blob, const int64_t *d_ids, int
  * d_sink: device, one uint32 the kernel may write (practically never does). */
 int nwc_stream_read(const void *d_buf, int64_t bytes, uint32_t *d_sink, void *stream);
 
+/* Measurement helper, not part of the method: the uncompressed baseline, a
+ * plain BF16 GEMV y = W x with fp32 accumulation and no decode.
+ *   d_w  device, n rows of BF16 patterns, row pitch ldw elements (ldw >= k,
+ *        a multiple of 8), 16-byte aligned.
+ *   d_x  device, k BF16 patterns, 16-byte aligned; 8 <= k <= 24576, k a
+ *        multiple of 8.  d_y: device, n fp32 outputs, 4-byte aligned.
+ * NWC_ERR_ARG for null or misaligned pointers, NWC_ERR_SHAPE otherwise. */
+int nwc_bf16_gemv(const void *d_w, int64_t n, int64_t k, int64_t ldw, const void *d_x, float *d_y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

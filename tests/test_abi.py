@@ -262,6 +262,19 @@ def test_launchers_reject_bad_arguments_before_any_gpu_call():
     assert L.nwc_matvec(h8.ctypes.data, fake, fake, None, fake, None, 0, None) == -1   # fp8 needs a scale
 
 
+def test_bf16_gemv_rejects_bad_arguments_before_any_gpu_call():
+    L = ctypes.CDLL(nwc.LIB_PATH)
+    L.nwc_bf16_gemv.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    fake = 1 << 20  # aligned, never dereferenced: every call below fails its checks first
+    assert L.nwc_bf16_gemv(None, 4, 64, 64, fake, fake, None) == -1
+    assert L.nwc_bf16_gemv(fake + 8, 4, 64, 64, fake, fake, None) == -1       # w not 16-byte aligned
+    assert L.nwc_bf16_gemv(fake, 4, 60, 64, fake, fake, None) == -2           # k not a multiple of 8
+    assert L.nwc_bf16_gemv(fake, 4, 64, 56, fake, fake, None) == -2           # ldw < k
+    assert L.nwc_bf16_gemv(fake, 4, 24576 + 8, 24584, fake, fake, None) == -2  # activations over the LDS limit
+    assert L.nwc_bf16_gemv(fake, 0, 64, 64, fake, fake, None) == -2
+
+
 def test_one_hip_runtime_whatever_the_import_order():
     # Loading the library before torch once put two HIP runtimes in the process
     # (PyTorch's bundled one and /opt/rocm's); the library's then saw no device.

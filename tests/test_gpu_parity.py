@@ -350,6 +350,22 @@ def test_prefill_equals_the_library_gemm_on_the_weights(tokens):
         P.prefill(dm, xt[:, :100])
 
 
+# ----------------------------------------------------------------- uncompressed reference GEMV
+@pytest.mark.parametrize("n,k,ld", [(300, 1000, 1000), (7, 24576, 24576), (33, 8, 16), (4097, 2560, 2568)])
+def test_bf16_gemv_reference(n, k, ld):
+    """The plain BF16 GEMV baseline meets the same bound against the oracle's float64 sum."""
+    print(f"case bf16_gemv n={n} k={k} ld={ld}", flush=True)
+    w = S.student_t_bf16(95, (n, k))
+    x = S.activation_bf16(96, k)
+    wp = np.zeros((n, ld), dtype=np.uint16)
+    wp[:, :k] = w
+    y = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+    nwc.bf16_gemv(dev16(wp), dev16(x), y)
+    torch.cuda.synchronize()
+    y_ref, A = O.matvec_bf16_ref(w, x)
+    check_tol(y.cpu().numpy().astype(np.float64), y_ref, A, "bf16 gemv")
+
+
 # ----------------------------------------------------------------- full-size workloads
 def _device_matrix(seed, n, k, sigma):
     wt = S.device_normal_bf16(seed, (n, k), sigma, DEV)

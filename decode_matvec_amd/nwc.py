@@ -145,6 +145,24 @@ def _dev(t):
     return 0 if t is None else t.data_ptr()
 
 
+def _need(fn: str, what: str, t, min_elems: int, elem_size: int, floating=None):
+    """Host-side check of a device tensor argument before its pointer reaches the library: a CUDA/HIP tensor,
+    contiguous, of the element size the entry point reads or writes, holding at least ``min_elems`` elements.
+    ``floating``: True requires a floating dtype (fp32 outputs, scales), False an integer one (ids)."""
+    if t is None:
+        raise ValueError(f"{fn}: {what} is required")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{fn}: {what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {what} must be contiguous")
+    if t.element_size() != elem_size:
+        raise ValueError(f"{fn}: {what} needs {elem_size}-byte elements, got {t.dtype}")
+    if floating is not None and t.dtype.is_floating_point != floating:
+        raise ValueError(f"{fn}: {what} has dtype {t.dtype}")
+    if t.numel() < min_elems:
+        raise ValueError(f"{fn}: {what} holds {t.numel()} elements, needs {min_elems}")
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -152,17 +170,39 @@ def _stream(stream):
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
+def _shape(header: np.ndarray):
+    """(n, k, elem) read from the host header copy (validated by the library on every call)."""
+    h = np.frombuffer(np.ascontiguousarray(header[:32]).tobytes(), dtype=np.uint8)
+    elem = int(h[8:12].view(np.uint32)[0])
+    n, k = (int(v) for v in h[16:32].view(np.int64))
+    return n, k, elem
+
+
 def matvec(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -> None:
     """y[n] (fp32) = W x (times scale for fp8) on the GPU; all device arguments are torch tensors."""
+    n, k, elem = _shape(header)
+    _need("nwc_matvec", "x", x, k, 2)
+    _need("nwc_matvec", "y", y, n, 4, floating=True)
+    if elem == NWC_FP8_E4M3:
+        _need("nwc_matvec", "scale", scale, n, 4, floating=True)
     _check("nwc_matvec", lib.nwc_matvec(_host_ptr(header), _dev(d_blob), _dev(x), _dev(scale), _dev(y), _dev(ws),
                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def matvec_batch(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -> None:
     """y[b] (fp32 rows) = W x[b] for the rows of x (batch x ldx BF16 patterns) into y (batch x ldy fp32)."""
+    n, k, elem = _shape(header)
+    if x.dim() != 2 or y.dim() != 2:
+        raise ValueError("nwc_matvec_batch: x and y must be 2-D (rows x elements)")
     batch = x.shape[0]
     if y.shape[0] != batch:
         raise ValueError("x and y need the same number of rows")
+    if x.shape[1] < k or y.shape[1] < n:
+        raise ValueError(f"nwc_matvec_batch: rows of x need >= {k} elements and rows of y >= {n}")
+    _need("nwc_matvec_batch", "x", x, batch * x.shape[1], 2)
+    _need("nwc_matvec_batch", "y", y, batch * y.shape[1], 4, floating=True)
+    if elem == NWC_FP8_E4M3:
+        _need("nwc_matvec_batch", "scale", scale, n, 4, floating=True)
     _check("nwc_matvec_batch", lib.nwc_matvec_batch(_host_ptr(header), _dev(d_blob), _dev(x), x.stride(0), batch,
                                                     _dev(scale), _dev(y), y.stride(0), _dev(ws),
                                                     0 if ws is None else ws.numel() * ws.element_size(),
@@ -170,6 +210,11 @@ def matvec_batch(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=N
 
 
 def dequant(header: np.ndarray, d_blob, out, ld: int, stream=None) -> None:
+    """Rows of the matrix into out (row i at element i*ld): BF16 patterns, or fp8 bytes."""
+    n, k, elem = _shape(header)
+    if ld < k:
+        raise ValueError(f"nwc_dequant: ld {ld} < k {k}")
+    _need("nwc_dequant", "out", out, (n - 1) * ld + k, 2 if elem == NWC_BF16 else 1)
     _check("nwc_dequant", lib.nwc_dequant(_host_ptr(header), _dev(d_blob), _dev(out), ld, _stream(stream)))
 
 
@@ -179,16 +224,28 @@ def stream_read(buf, sink, nbytes=None, stream=None) -> None:
     _check("nwc_stream_read", lib.nwc_stream_read(_dev(buf), n, _dev(sink), _stream(stream)))
 
 
-def bf16_gemv(w, x, y, stream=None) -> None:
-    """Plain BF16 GEMV y = W x (the uncompressed measurement baseline): w int16/bfloat16 [n, ldw] device,
-    x [k] device, y fp32 [n] device."""
+def bf16_gemv(w, x, y, stream=None, k=None) -> None:
+    """Plain BF16 GEMV y = W x (the uncompressed measurement baseline): w int16/bfloat16 [n, ldw] device
+    (row pitch w.stride(0)), x [k] device, y fp32 [n] device.  k defaults to w.shape[1]."""
+    if w.dim() != 2:
+        raise ValueError("nwc_bf16_gemv: w must be 2-D")
     n, ldw = w.shape
-    k = x.numel()
-    _check("nwc_bf16_gemv", lib.nwc_bf16_gemv(_dev(w), n, k, w.stride(0) if w.dim() == 2 else ldw, _dev(x), _dev(y),
+    k = ldw if k is None else int(k)
+    if k > ldw:
+        raise ValueError(f"nwc_bf16_gemv: k {k} > columns of w {ldw}")
+    if w.element_size() != 2 or not w.is_cuda or w.stride(1) != 1:
+        raise ValueError("nwc_bf16_gemv: w must be a device tensor of 2-byte elements with unit column stride")
+    _need("nwc_bf16_gemv", "x", x, k, 2)
+    _need("nwc_bf16_gemv", "y", y, n, 4, floating=True)
+    _check("nwc_bf16_gemv", lib.nwc_bf16_gemv(_dev(w), n, k, w.stride(0), _dev(x), _dev(y),
                                               _stream(stream)))
 
 
 def gather(header: np.ndarray, d_blob, ids, out, stream=None) -> None:
+    """Rows ids[t] of the matrix into out[t] (k elements each); ids outside [0, n) give zero rows."""
+    n, k, elem = _shape(header)
+    _need("nwc_gather", "ids", ids, 0, 8, floating=False)
+    _need("nwc_gather", "out", out, ids.numel() * k, 2 if elem == NWC_BF16 else 1)
     _check("nwc_gather", lib.nwc_gather(_host_ptr(header), _dev(d_blob), _dev(ids), ids.numel(), _dev(out),
                                         _stream(stream)))
 

@@ -287,3 +287,55 @@ def test_one_hip_runtime_whatever_the_import_order():
     assert out.returncode == 0, out.stderr
     paths = eval(out.stdout.strip().splitlines()[-1])
     assert len(paths) == 1, paths
+
+
+class _FakeDev:
+    """Stands in for a device tensor in host-side argument checks (never dereferenced)."""
+
+    def __init__(self, numel, esize, floating=False, contiguous=True, cuda=True):
+        import torch
+        self._n, self._e, self.is_cuda, self._c = numel, esize, cuda, contiguous
+        self.dtype = {(4, True): torch.float32, (4, False): torch.int32, (2, False): torch.int16,
+                      (2, True): torch.bfloat16, (1, False): torch.uint8, (8, False): torch.int64}[(esize, floating)]
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        raise AssertionError("the binding passed a rejected tensor on to the library")
+
+
+def test_binding_checks_tensor_arguments_on_the_host():
+    w = S.normal_bf16(5, (70, 100), 0.02)
+    hdr = nwc.encode(w)[:256].copy()
+    blob = _FakeDev(1 << 20, 1)
+    ok_x, ok_y = _FakeDev(100, 2), _FakeDev(70, 4, True)
+    bad = [("x short", _FakeDev(99, 2), ok_y), ("x 4-byte", _FakeDev(100, 4, True), ok_y),
+           ("x on host", _FakeDev(100, 2, cuda=False), ok_y), ("x strided", _FakeDev(100, 2, contiguous=False), ok_y),
+           ("y short", ok_x, _FakeDev(69, 4, True)), ("y int", ok_x, _FakeDev(70, 4, False)),
+           ("y bf16", ok_x, _FakeDev(70, 2, True))]
+    for what, x, y in bad:
+        with pytest.raises(ValueError):
+            nwc.matvec(hdr, blob, x, y)
+    with pytest.raises(ValueError):   # dequant output too small for (n-1)*ld + k elements
+        nwc.dequant(hdr, blob, _FakeDev(69 * 128 + 99, 2), 128)
+    with pytest.raises(ValueError):   # ld < k
+        nwc.dequant(hdr, blob, _FakeDev(70 * 128, 2), 99)
+    with pytest.raises(ValueError):   # fp8 bytes expected for an fp8 blob, not BF16
+        q, _ = S.fp8_quantize(w)
+        nwc.dequant(nwc.encode(q, elem=1)[:256].copy(), blob, _FakeDev(70 * 100, 2), 100)
+    with pytest.raises(ValueError):   # ids must be int64
+        nwc.gather(hdr, blob, _FakeDev(4, 4, False), _FakeDev(400, 2))
+    ids = _FakeDev(4, 8)
+    with pytest.raises(ValueError):   # out must hold n_ids * k elements
+        nwc.gather(hdr, blob, ids, _FakeDev(399, 2))
+    q, _ = S.fp8_quantize(w)
+    h8 = nwc.encode(q, elem=1)[:256].copy()
+    with pytest.raises(ValueError):   # fp8 needs n fp32 scales
+        nwc.matvec(h8, blob, ok_x, ok_y, scale=_FakeDev(69, 4, True))

@@ -66,8 +66,8 @@ def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16, fused=False):
         dense = {}
         for idx, (name, n, k) in enumerate(C.QWEN3_4B):
             ws, xs = C.qwen3_seed(layer, idx)
-            wt = S.device_normal_bf16(ws, (n, k), np.float32(C.sigma_for(k)), dev)
-            w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+            w = S.blocked_normal_bf16(ws, (n, k), np.float32(C.sigma_for(k)))
+            wt = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) if with_bf16 else None
             blob = nwc.encode(w)
             dm = nwc.DeviceMatrix(blob, dev)
             x = S.activation_bf16(xs, k)
@@ -154,8 +154,8 @@ def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16, with_fused=False
     t0 = time.time()
 
     def one(seed, n, k):
-        wt = S.device_normal_bf16(seed, (n, k), np.float32(C.sigma_for(k)), dev)
-        w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+        w = S.blocked_normal_bf16(seed, (n, k), np.float32(C.sigma_for(k)))
+        wt = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) if with_bf16 else None
         dm = nwc.DeviceMatrix(nwc.encode(w), dev)
         return dict(dm=dm, n=n, k=k, y=torch.empty(n, dtype=torch.float32, device=dev),
                     w_bf16=wt if with_bf16 else None, w_host=w if with_fused else None,
@@ -333,8 +333,8 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
     and the fp8 e4m3 variant: the 1024 x 1024 matrix and 9728 x 2560 matrices."""
     F = torch.nn.functional
     n, k = C.EMBED_VOCAB, C.EMBED_HIDDEN
-    wt = S.device_normal_bf16(C.EMBED["w_seed"], (n, k), 0.02, dev)
-    w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
+    w = S.blocked_normal_bf16(C.EMBED["w_seed"], (n, k), 0.02)
+    wt = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16)
     dm = nwc.DeviceMatrix(nwc.encode(w), dev)
     del w
     x = torch.from_numpy(S.activation_bf16(C.EMBED["x_seed"], k).view(np.int16)).to(dev)
@@ -380,8 +380,7 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
             if fn_ == 1024:
                 wf = S.normal_bf16(sd, (fn_, fk), C.SINGLE["sigma"])
             else:
-                wf = S.device_normal_bf16(sd, (fn_, fk), np.float32(C.sigma_for(fk)), dev)
-                wf = wf.view(torch.int16).cpu().numpy().view(np.uint16)
+                wf = S.blocked_normal_bf16(sd, (fn_, fk), np.float32(C.sigma_for(fk)))
             q, sc = S.fp8_quantize(wf)
             dms.append(nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), dev))
             scs.append(torch.from_numpy(sc).to(dev))

@@ -10,10 +10,15 @@ Recipes (all seeds fixed; see ``configs``):
 
 * weights: fp32 standard normal draws times an fp32 standard deviation, rounded
   to BF16 with round-to-nearest-even; activations likewise with sigma 1.
-* small matrices use numpy's PCG64 ``default_rng(seed)`` on the host;
-  multi-hundred-megabyte matrices use torch's device generator (Philox) on the
-  GPU with the same seed, because host generation of billions of draws takes
-  minutes.  Which generator a matrix uses is part of its recipe.
+* small matrices (the 1024 x 1024 matrix, the odd shapes) draw the whole
+  matrix in row-major order from numpy's PCG64 ``default_rng(seed)``;
+  the workload matrices of the decoder layer sets and the embedding tables
+  draw in blocks of 256 rows, block b from
+  ``Generator(PCG64(SeedSequence(seed, spawn_key=(b,))))`` (the b-th child of
+  ``SeedSequence(seed).spawn``), so that the blocks of billions of draws can be
+  made on several host threads and every consumer -- the CPU oracle tests, the
+  GPU tests, the benchmark -- sees the same matrices.  Which recipe a matrix
+  uses is part of its workload definition (``synth.configs``).
 * heavy-tailed weights: 0.02 times a Student-t draw with 3 degrees of freedom.
 * rare values are injected at seeded positions to exercise the escape code.
 * fp8 weights: symmetric per-output-channel absmax scaling to the e4m3fn range,
@@ -26,7 +31,7 @@ import numpy as np
 __all__ = [
     "bf16_from_f32", "f32_from_bf16", "normal_bf16", "student_t_bf16", "inject_rare",
     "all_patterns_bf16", "all_bytes_fp8", "fp8_quantize", "token_ids", "activation_bf16",
-    "device_normal_bf16",
+    "blocked_normal_bf16", "BLOCK_ROWS", "odd_shape_matrix",
 ]
 
 
@@ -129,13 +134,43 @@ def token_ids(seed: int, vocab: int, n: int) -> np.ndarray:
     return np.random.default_rng(seed).integers(0, vocab, size=n, dtype=np.int64)
 
 
-def device_normal_bf16(seed: int, shape, sigma: float, device="cuda"):
-    """torch bf16 tensor of N(0, sigma) draws made by torch's generator on ``device``.
+BLOCK_ROWS = 256
 
-    fp32 draws times fp32(sigma), then a round-to-nearest-even cast to bf16."""
-    import torch
-    g = torch.Generator(device=device)
-    g.manual_seed(int(seed))
-    z = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
-    z.mul_(float(np.float32(sigma)))
-    return z.to(torch.bfloat16)
+
+def blocked_normal_bf16(seed: int, shape, sigma: float, threads: int | None = None) -> np.ndarray:
+    """BF16 bits of fp32 N(0, sigma) draws, rows drawn in blocks of BLOCK_ROWS.
+
+    Block b (rows [256 b, 256 b + 256)) is drawn row-major from
+    ``Generator(PCG64(SeedSequence(seed, spawn_key=(b,))))``: fp32 standard
+    normal draws times fp32(sigma), then round-to-nearest-even to BF16.  The
+    result does not depend on ``threads``."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    n, k = shape
+    out = np.empty((n, k), np.uint16)
+    sig = np.float32(sigma)
+
+    def one(b):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(int(seed), spawn_key=(b,))))
+        r0, r1 = b * BLOCK_ROWS, min(n, (b + 1) * BLOCK_ROWS)
+        z = g.standard_normal((r1 - r0, k), dtype=np.float32)
+        z *= sig
+        out[r0:r1] = bf16_from_f32(z)
+
+    nb = (n + BLOCK_ROWS - 1) // BLOCK_ROWS
+    with ThreadPoolExecutor(max(1, min(nb, threads or os.cpu_count() or 1))) as ex:
+        list(ex.map(one, range(nb)))
+    return out
+
+
+def odd_shape_matrix(idx: int, kind: str):
+    """The odd-shape workload's matrix ``idx`` of kind "normal" (N(0, 0.02)) or
+    "t3" (0.02 t3), with rare values injected; returns (w, x, seed).
+
+    Seed 300000 + 2 idx (+1 for t3); rare positions from seed + 50; the
+    activation from seed + 60."""
+    from . import configs as C
+    n, k = C.ODD_SHAPES[idx]
+    seed = C.odd_seed(2 * idx + (kind == "t3"))
+    w = normal_bf16(seed, (n, k), 0.02) if kind == "normal" else student_t_bf16(seed, (n, k))
+    return inject_rare(w, seed + 50), activation_bf16(seed + 60, k), seed

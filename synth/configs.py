@@ -10,6 +10,11 @@
   4096 uniform token ids; and an fp8 e4m3 copy of the 1024 x 1024 matrix.
 * ``qwen25_7b_step``: 28 Qwen2.5-7B-shaped layers plus a 152064 x 3584 lm_head,
   all N(0, 1/sqrt(K)).
+
+The matrices of the layer sets, the step and the embedding table are drawn
+with ``synth.blocked_normal_bf16`` (256-row blocks, one PCG64 stream per block);
+the 1024 x 1024 matrix, the odd shapes and every activation with numpy's
+``default_rng(seed)`` over the whole array.
 """
 from __future__ import annotations
 
@@ -51,6 +56,37 @@ def qwen25_seed(layer: int, idx: int) -> int:
 
 QWEN25_LM_HEAD_SEED = 500999
 QWEN25_X_SEED = 501000
+
+
+def qwen25_x_seed(layer: int, idx: int) -> int:
+    """Activation seed of matrix ``idx`` of ``layer`` when it is checked on its own (lm_head: idx 99, layer 0)."""
+    return 600000 + 10 * layer + idx
+
+
+def qwen3_matrices(layers: int = QWEN3_4B_LAYERS):
+    """Every matrix of the Qwen3-4B layer set, in layer order: dicts of name, layer, n, k, sigma, seeds."""
+    for layer in range(layers):
+        for idx, (name, n, k) in enumerate(QWEN3_4B):
+            ws, xs = qwen3_seed(layer, idx)
+            yield dict(label=f"qwen3_4b.L{layer}.{name}", name=name, layer=layer, n=n, k=k, sigma=sigma_for(k),
+                       w_seed=ws, x_seed=xs)
+
+
+def qwen25_matrices(layers: int = QWEN25_7B_LAYERS, lm_head: bool = True):
+    """Every matrix of the Qwen2.5-7B step (layers, then the lm_head)."""
+    for layer in range(layers):
+        for idx, (name, n, k) in enumerate(QWEN25_7B):
+            yield dict(label=f"qwen25_7b.L{layer}.{name}", name=name, layer=layer, n=n, k=k, sigma=sigma_for(k),
+                       w_seed=qwen25_seed(layer, idx), x_seed=qwen25_x_seed(layer, idx))
+    if lm_head:
+        yield dict(label="qwen25_7b.lm_head", name="lm_head", layer=layers, n=QWEN25_7B_VOCAB, k=QWEN25_7B_HIDDEN,
+                   sigma=sigma_for(QWEN25_7B_HIDDEN), w_seed=QWEN25_LM_HEAD_SEED, x_seed=qwen25_x_seed(0, 99))
+
+
+def embedding_matrix():
+    """The tied embedding / lm_head table of the embedding workload."""
+    return dict(label="tied_embedding", name="embed", layer=0, n=EMBED_VOCAB, k=EMBED_HIDDEN, sigma=0.02,
+                w_seed=EMBED["w_seed"], x_seed=EMBED["x_seed"])
 
 
 def odd_seed(index: int) -> int:

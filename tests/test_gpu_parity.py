@@ -2,10 +2,8 @@
 
 Decode (dequant) and gather must be bit-exact; the matvec must satisfy
 |y - y_ref| <= 1e-3 * sum_j |w_ij x_j| + 1e-6 per output, y_ref the oracle's
-float64 sum.  Small workloads are checked element by element; the full-size
-workloads are checked on every dequantized element (against the oracle's
-lossless decode, which is the input) and on sampled matvec outputs that the
-oracle computes one by one.
+float64 sum.  Small workloads are checked element by element; every matrix of
+the full-size workloads is checked on every element in test_gpu_workloads.py.
 """
 import numpy as np
 import pytest
@@ -163,10 +161,7 @@ def _odd_cases():
 
 @pytest.mark.parametrize("idx,n,k,kind", _odd_cases())
 def test_odd_shapes(idx, n, k, kind):
-    seed = C.odd_seed(2 * idx + (kind == "t3"))
-    w = S.normal_bf16(seed, (n, k), 0.02) if kind == "normal" else S.student_t_bf16(seed, (n, k))
-    w = S.inject_rare(w, seed + 50)
-    x = S.activation_bf16(seed + 60, k)
+    w, x, _ = S.odd_shape_matrix(idx, kind)
     full_parity_bf16(w, x)
 
 
@@ -367,62 +362,8 @@ def test_bf16_gemv_reference(n, k, ld):
 
 
 # ----------------------------------------------------------------- full-size workloads
-def _device_matrix(seed, n, k, sigma):
-    wt = S.device_normal_bf16(seed, (n, k), sigma, DEV)
-    w = wt.view(torch.int16).cpu().numpy().view(np.uint16)
-    return wt, w
-
-
-def _sampled_matvec(dm, w, x, rows):
-    y = run_matvec(dm, x)
-    y_ref, A = O.matvec_bf16_ref(w[rows], x)
-    check_tol(y[rows], y_ref, A, f"sampled {w.shape}")
-    return y
-
-
-def _check_big(wt, w, seed, nsample=96):
-    n, k = w.shape
-    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
-    out = torch.empty((n, k), dtype=torch.int16, device=DEV)
-    dm.dequant(out)
-    assert torch.equal(out, wt.view(torch.int16)), "dequant differs from the input"
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, nsample)]))
-    enc_rows = O.encode_bf16(w[rows[:6]])      # oracle decode of a few sampled rows
-    assert np.array_equal(O.decode_bf16(enc_rows), w[rows[:6]])
-    x = S.activation_bf16(seed + 1, k)
-    _sampled_matvec(dm, w, x, rows)
-    return dm
-
-
-def test_qwen3_4b_one_layer_full_size():
-    for idx, (name, n, k) in enumerate(C.QWEN3_4B):
-        ws, xs = C.qwen3_seed(0, idx)
-        print(f"qwen3 layer0 {name} {n}x{k}", flush=True)
-        wt, w = _device_matrix(ws, n, k, np.float32(C.sigma_for(k)))
-        _check_big(wt, w, xs)
-
-
-def test_tied_embedding_gather_and_lm_head():
-    n, k = C.EMBED_VOCAB, C.EMBED_HIDDEN
-    wt, w = _device_matrix(C.EMBED["w_seed"], n, k, 0.02)
-    dm = nwc.DeviceMatrix(nwc.encode(w), DEV)
-    ids = S.token_ids(C.EMBED["ids_seed"], n, C.N_IDS)
-    ids[:3] = [0, n - 1, ids[5]]
-    out = torch.empty((len(ids), k), dtype=torch.int16, device=DEV)
-    dm.gather(torch.from_numpy(ids).to(DEV), out)
-    torch.cuda.synchronize()
-    assert torch.equal(out, wt.view(torch.int16)[torch.from_numpy(ids).to(DEV)])
-    x = S.activation_bf16(C.EMBED["x_seed"], k)
-    rows = np.unique(np.random.default_rng(3).integers(0, n, 256))
-    _sampled_matvec(dm, w, x, rows)
-
-
-def test_qwen25_7b_matrices_sampled():
-    for idx, (name, n, k) in enumerate(C.QWEN25_7B):
-        print(f"qwen2.5 layer0 {name} {n}x{k}", flush=True)
-        wt, w = _device_matrix(C.qwen25_seed(0, idx), n, k, np.float32(C.sigma_for(k)))
-        _check_big(wt, w, C.qwen25_seed(0, idx) + 7, nsample=32)
+# Every matrix of the full-size workloads is checked element by element in
+# test_gpu_workloads.py; here the decode step's wiring.
 
 
 def test_qwen25_step_two_layers_matches_bf16_stack():

@@ -19,18 +19,19 @@ import synth as S
 from synth import configs as C
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "bf16_tiny_codes.txt")
+GOLDEN_FP8 = os.path.join(os.path.dirname(__file__), "golden", "fp8_tiny_codes.txt")
 
 
-def _load_golden():
+def load_golden(path=GOLDEN, dtype=np.uint16):
     ex = {}
-    lines = [l.strip() for l in open(GOLDEN) if l.strip() and not l.startswith("#")]
+    lines = [l.strip() for l in open(path) if l.strip() and not l.startswith("#")]
     i = 0
     while i < len(lines):
         parts = lines[i].split()
         if parts[0] == "matrix":
             name, n, k = parts[1], int(parts[2]), int(parts[3])
             rows = [[int(v, 16) for v in lines[i + 1 + r].split()] for r in range(n)]
-            ex.setdefault(name, {})["w"] = np.array(rows, dtype=np.uint16)
+            ex.setdefault(name, {})["w"] = np.array(rows, dtype=dtype)
             i += 1 + n
             continue
         if parts[0] == "ranks":
@@ -46,7 +47,7 @@ def _load_golden():
 # --------------------------------------------------------------- worked example
 @pytest.mark.parametrize("name", ["A", "B"])
 def test_golden_bitstreams(name):
-    ex = _load_golden()[name]
+    ex = load_golden()[name]
     enc_s = O.encode_bf16_scalar(ex["w"])
     enc_v = O.encode_bf16(ex["w"])
     assert list(enc_s["rank_to_sym"][:len(ex["ranks"])]) == ex["ranks"]
@@ -312,13 +313,54 @@ def test_fp8_matvec_exact_rationals():
         assert abs(Fraction(float(A[i])) - Ae) <= 200 * Fraction(2) ** -51 * Ae
 
 
-# --------------------------------------------------------------- whole workloads
-@pytest.mark.skipif(not os.environ.get("NWC_SLOW_ORACLE"),
-                    reason="36 x 7 full-size oracle round trips take hours on one core; set NWC_SLOW_ORACLE=1")
-def test_qwen3_layer_roundtrip_all():
-    for layer in range(C.QWEN3_4B_LAYERS):
-        for idx, (_, n, k) in enumerate(C.QWEN3_4B):
-            ws, _ = C.qwen3_seed(layer, idx)
-            w = S.normal_bf16(ws, (n, k), C.sigma_for(k))
-            enc = O.encode_bf16(w)
-            assert np.array_equal(O.decode_bf16(enc), w)
+def test_fp8_golden_bitstreams():
+    ex = load_golden(GOLDEN_FP8, np.uint8)["C"]
+    enc = O.encode_fp8(ex["w"])
+    assert list(enc["rank_to_sym"][:len(ex["ranks"])]) == ex["ranks"]
+    for r, bits in ex["rowbits"].items():
+        off, nb = enc["row_off"][r], enc["row_bits"][r]
+        assert list(enc["bits"][off:off + nb]) == bits
+        # the same bits, codeword by codeword, from the codeword definition
+        cw = []
+        for b in ex["w"][r]:
+            b = int(b)
+            cw += O.codeword_fp8(int(enc["sym_to_rank"][(b >> 3) & 15]), b >> 7, (b >> 3) & 15, b & 7)
+        assert cw == bits
+    assert enc["coded_bits"] == ex["coded"]
+    assert np.array_equal(O.decode_fp8(enc), ex["w"])
+
+
+def test_fp8_kraft_and_prefix_free():
+    # Symbol part (sign and the 3 raw mantissa bits excluded, both fixed-width):
+    # ranks 0..7 are 1..8 bits, the 8 escaped fields 12 bits (8 ones + E).
+    from fractions import Fraction
+    r2s = np.arange(16)
+    kraft = sum(Fraction(1, 2 ** (O.code_length_fp8(r) - 4)) for r in range(16))
+    assert kraft == 1 - Fraction(1, 2 ** 8) + 8 * Fraction(1, 2 ** 12)
+    assert kraft <= 1
+    words = {}
+    for b in range(256):
+        s_, E, M = b >> 7, (b >> 3) & 15, b & 7
+        w = tuple(O.codeword_fp8(int(np.where(r2s == E)[0][0]), s_, E, M))
+        assert len(w) == O.code_length_fp8(E)
+        assert w not in words
+        words[w] = b
+    ws = list(words)
+    for a in ws:
+        for c in ws:
+            if a is not c:
+                assert a != c[:len(a)], "fp8 codeword is a prefix of another"
+
+
+def test_fp8_coded_bits_against_byte_entropy():
+    # The whole-byte code against the byte's Shannon entropy on the fp8 copy of
+    # the 1024 x 1024 matrix: above the bound (any prefix code is), and the
+    # gap is what a code over whole bytes could still save (reported).
+    w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
+    q, _ = S.fp8_quantize(w)
+    enc = O.encode_fp8(q)
+    h = O.byte_entropy(q)
+    per = enc["coded_bits"] / q.size
+    print(f"fp8 1024x1024: H(byte) {h:.4f} bits, coded {per:.4f} bits ({per / h - 1:+.2%}), "
+          f"{per / 8:.4f} of the fp8 bytes", flush=True)
+    assert h <= per <= h + 1

@@ -355,7 +355,7 @@ def test_bf16_gemv_reference(n, k, ld):
     wp = np.zeros((n, ld), dtype=np.uint16)
     wp[:, :k] = w
     y = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
-    nwc.bf16_gemv(dev16(wp), dev16(x), y)
+    nwc.bf16_gemv(dev16(wp), dev16(x), y, k=k)
     torch.cuda.synchronize()
     y_ref, A = O.matvec_bf16_ref(w, x)
     check_tol(y.cpu().numpy().astype(np.float64), y_ref, A, "bf16 gemv")

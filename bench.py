@@ -724,9 +724,25 @@ def main():
     mats, fmats = build_layer_set(torch, nwc, S, C, dev, args.layers,
                                   not args.no_bf16_baseline and not args.profile_sweeps,
                                   fused=not (args.profile_sweeps or args.no_fused))
-    n_launch = len(mats)
+    # The step as a decoder can launch it: in each layer the projections that
+    # read one input (q, k, v; gate, up) run as one nwc_matvec_group launch, o
+    # and down alone, in layer order -- 4 launches per layer.  Each matrix keeps
+    # its own encoding and its own activation.
+    by_layer = [{m["name"]: m for m in mats[7 * l:7 * l + 7]} for l in range(args.layers)]
+    launch_groups = [[L[p] for p in parts] for L in by_layer for _, parts in FUSED_QWEN3]
+    n_launch = len(launch_groups)
+
+    def run_group(g):
+        if len(g) == 1:
+            g[0]["dm"].matvec(g[0]["x"], g[0]["y"])
+        else:
+            nwc.matvec_group([m["dm"] for m in g], [m["x"] for m in g], [m["y"] for m in g])
 
     def sweep():
+        for g in launch_groups:
+            run_group(g)
+
+    def sweep_per_matrix():
         for m in mats:
             m["dm"].matvec(m["x"], m["y"])
 
@@ -738,13 +754,22 @@ def main():
             dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        for _ in range(args.profile_sweeps):
-            sweep()
+        # The timed step's launches only: the sweep captured once and replayed.
+        pg = torch.cuda.CUDAGraph()
+        sweep()
         torch.cuda.synchronize()
-        print(json.dumps({"profile_sweeps": args.profile_sweeps, "matvecs_per_sweep": n_launch,
-                          "algo_bytes_per_matvec": sum(m["algo_bytes"] for m in mats) / n_launch,
-                          "blob_bytes_per_matvec": sum(m["blob_bytes"] for m in mats) / n_launch,
-                          "weights_per_matvec": sum(m["n"] * m["k"] for m in mats) / n_launch,
+        with torch.cuda.graph(pg):
+            sweep()
+        for _ in range(args.profile_sweeps):
+            pg.replay()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_sweeps": args.profile_sweeps, "launches_per_sweep": n_launch,
+                          "matvecs_per_sweep": len(mats),
+                          "algo_bytes_per_launch": sum(m["algo_bytes"] for m in mats) / n_launch,
+                          "blob_bytes_per_launch": sum(m["blob_bytes"] for m in mats) / n_launch,
+                          "weights_per_launch": sum(m["n"] * m["k"] for m in mats) / n_launch,
+                          "per_group_algo_bytes": {gname: sum(m["algo_bytes"] for m in launch_groups[i])
+                                                   for i, (gname, _) in enumerate(FUSED_QWEN3)},
                           "copy_calibration_bytes": (64 << 20) * 4 if args.copy_calibration else 0,
                           "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
@@ -753,6 +778,14 @@ def main():
     # step from Python would otherwise be limited by host launch overhead,
     # not by the GPU.  The eager (per-call ctypes launch) rate is reported too.
     ms_eager = time_region(torch, sweep, max(2, args.steps // 4), 1)
+    # One launch per matrix (252 per sweep), for comparison.
+    sweep_per_matrix()
+    torch.cuda.synchronize()
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        sweep_per_matrix()
+    ms_one = time_region(torch, g1.replay, args.steps, args.warmup)
+    del g1
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -790,6 +823,23 @@ def main():
                            "bits_per_weight_coded": round(group[0]["info"]["coded_bits"] / (n * k), 4),
                            "bits_per_weight_blob": round(group[0]["blob_bytes"] * 8 / (n * k), 4),
                            "geometry": {f: group[0]["info"][f] for f in ("cols_per_lane", "rows_per_wave", "waves_per_group", "n_spans")}}
+
+    # Each launch of the grouped step on its own: the 36 launches of one kind
+    # (q,k,v group / o / gate,up group / down) replayed back to back.
+    per_launch = {}
+    for gi, (gname, parts) in enumerate(FUSED_QWEN3):
+        gl = launch_groups[gi::len(FUSED_QWEN3)]
+        gg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gg):
+            for g in gl:
+                run_group(g)
+        gms = time_region(torch, gg.replay, max(3, args.steps // 2), 1)
+        us = gms * 1e3 / len(gl)
+        gb = sum(m["algo_bytes"] for g in gl for m in g) / len(gl)
+        bb = sum(m["blob_bytes"] for g in gl for m in g) / len(gl)
+        per_launch[gname] = {"matrices": list(parts), "us": round(us, 3), "algo_MB": round(gb / 1e6, 3),
+                             "blob_MB": round(bb / 1e6, 3), "compressed_GBps": round(gb / (us * 1e-6) / 1e9, 1),
+                             "blob_GBps": round(bb / (us * 1e-6) / 1e9, 1)}
 
     # Decode clocks per 64 weights: CU-clocks (time x MI355X's 2.4 GHz peak engine
     # clock x 256 CUs) over weights / 64, for the cold sweep and for one gate
@@ -876,6 +926,9 @@ def main():
                               "kernel": "nwc_bf16_gemv: plain BF16 GEMV, 16-byte streaming loads, no decode"}
         del ys
 
+    # The dominant kernel is the fused decode + matvec (the group launches and
+    # the single-matrix launches run the same kernel body): algorithmic bytes
+    # per launch over its average launch time in the timed step.
     algo_per_launch = algo / n_launch
     achieved = algo_per_launch / (ms * 1e-3 / n_launch) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -890,13 +943,20 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1/sqrt(K)) BF16 weights)",
-        "config": {"workload": "qwen3_4b_layer_set", "layers": args.layers, "matrices": n_launch,
-                   "batch": 1, "note": "36 x {q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, "
-                                       "down 2560x9728}, cold rotation"},
+        "config": {"workload": "qwen3_4b_layer_set", "layers": args.layers, "matrices": len(mats),
+                   "launches": n_launch, "batch": 1,
+                   "note": "36 x {q 4096x2560, k/v 1024x2560, o 2560x4096, gate/up 9728x2560, down 2560x9728}, "
+                           "each matrix its own encoding and activation; per layer q,k,v one grouped launch, o, "
+                           "gate,up one grouped launch, down (nwc_matvec_group / nwc_matvec); cold rotation"},
         "us_per_layer": round(ms * 1e3 / args.layers, 2),
         "timing": "HIP graph replay of the whole sweep on one stream; HIP events around the timed steps",
+        "one_launch_per_matrix": {"ms_per_sweep": round(ms_one, 4), "launches": len(mats),
+                                  "us_per_layer": round(ms_one * 1e3 / args.layers, 2),
+                                  "GBps": round(algo / (ms_one * 1e-3) / 1e9, 1),
+                                  "hbm_frac_compressed": round(algo / (ms_one * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "per_launch": per_launch,
         "ms_per_step_eager_launches": round(ms_eager, 4),
-        "us_per_matvec_avg": round(ms * 1e3 / n_launch, 3),
+        "us_per_launch_avg": round(ms * 1e3 / n_launch, 3),
         "hbm_frac_compressed": round(value / HBM_PEAK_GBPS, 4),
         "effective_bf16_GBps": round(bf16_bytes / (ms * 1e-3) / 1e9, 1),
         "blob_GBps": round(blob / (ms * 1e-3) / 1e9, 1),

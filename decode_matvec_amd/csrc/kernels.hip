@@ -41,6 +41,12 @@
 
 #include "nwc_check.h"
 
+static_assert(offsetof(nwc_header_t, n) == 16 && offsetof(nwc_header_t, k) == 24 &&
+                  offsetof(nwc_header_t, rows_per_wave) == 36 && offsetof(nwc_header_t, n_rowgroups) == 48 &&
+                  offsetof(nwc_header_t, max_rows) == 56 && offsetof(nwc_header_t, off_mant) == 88 &&
+                  offsetof(nwc_header_t, off_code) == 96 && offsetof(nwc_header_t, rank_to_sym) == 128,
+              "header word offsets read by the group kernel");
+
 namespace {
 
 constexpr int kWavesPerCu = 25;  // persistent grids: waves per compute unit
@@ -513,28 +519,41 @@ __device__ __forceinline__ void load_x_slice(const uint16_t *__restrict__ x, uin
 // waves otherwise wait up to ~2.5 us for their arguments through the scalar
 // cache.  The buffers are __restrict__, so the compiler may read the item
 // table through the scalar cache.
+// The decode table into LDS, 1 KiB per direct load; wave w of W copies
+// pieces w, w + W, ...  Issued first by every matvec workgroup: nothing it
+// needs has to arrive before.
+__device__ __forceinline__ void stage_lut(const uint8_t *lut, uint32_t *s_lut, uint32_t W, uint32_t wave,
+                                          uint32_t lane) {
+  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += W)
+    dma_1k(lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
+}
+
+// The body of a matvec workgroup: `first` is its index among the `grid`
+// workgroups that share this matrix; off0/rows0 are this wave's first
+// item-table entry, which the caller reads before calling (scalar loads issued
+// before the decode table's copy; the body waits for them right after it).
+// The table copy is issued here, where `lut`, `items` and `code` are
+// restrict-qualified: the compiler then knows that the copy does not write the
+// item table and keeps the item-table reads in the loop scalar loads.  s_lut: the static decode table (and
+// fp8 escape table); s_dyn: one code region per wave, then groups_cap slots of
+// W*R row sums (matvec_lds on the host sizes it).
 template <bool FP8, int NG, bool SPLIT, int B>
-__global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
-                                                      const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
-                                                      uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t k,
-                                                      uint32_t log2S, const MvArgs a,
-                                                      const float *__restrict__ scale, float *__restrict__ y,
-                                                      float *__restrict__ partial) {
+__device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
+                                            const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
+                                            uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t first, uint32_t k,
+                                            uint32_t log2S, const MvArgs &a, const float *__restrict__ scale,
+                                            float *__restrict__ y, float *__restrict__ partial, uint32_t *s_lut,
+                                            uint32_t *s_dyn, uint32_t off0, uint32_t rows0) {
   constexpr uint32_t C = 16 * NG;
   // Code rows fetched ahead: a BF16 item's rows and its guard rows, typically;
   // an fp8 item (6.75 bits per weight) takes 4 to 6 rows of 16-column slices.
   constexpr int PR = FP8 ? 2 * NG + 4 : 2 * NG + 2;
   constexpr uint32_t kWinMax = FP8 ? 6u : 4u;  // longest item decoded from registers
-  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
-  // Dynamic LDS: one code region per wave, then groups_cap slots of W*R row
-  // sums (matvec_lds on the host sizes it).
-  extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Workgroup b takes groups b, b + grid, b + 2*grid, ...: at any time the
   // workgroups read neighbouring items, so the machine streams the planes in
   // order.
-  const uint32_t first = blockIdx.x;  // grid == gridDim.x
   const uint32_t n_mine = (n_groups - first + grid - 1) / grid;
   const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
   const uint32_t region_rows = a.region_words >> 6;
@@ -543,8 +562,12 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
   const uint32_t r = lane >> log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
   const bool row_lane = (lane & (S - 1u)) == S - 1u;
 
-  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += W)
-    dma_1k(lut + p * 1024, lds_addr(s_lut) + p * 1024, 1024, lane);
+  stage_lut(lut, s_lut, W, wave, lane);
+  // Waits for the first item-table entry (and whatever else the caller read
+  // before this) here, once, right after the table copy is issued, instead of
+  // where the compiler would put the first use (after the activation loads,
+  // one memory round trip later).
+  asm volatile("" ::"s"(off0), "s"(rows0));
   if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
@@ -552,7 +575,7 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
   X16 xv[B][NG];
   load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
   uint32_t ahead[PR];
-  fetch_code_ahead<PR>(code, items[2 * (first * W + wave)], items[2 * (first * W + wave) + 1], lane, ahead);
+  fetch_code_ahead<PR>(code, off0, rows0, lane, ahead);
   wait_vm0();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
@@ -645,6 +668,114 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
     const uint32_t grp = first + i * grid, grow = SPLIT ? grp / a.n_spans : grp;
     store_out<FP8, SPLIT>(a, grow * a.R + rr, grp - grow * a.n_spans, sum, scale, y, partial, b);
   }
+}
+
+template <bool FP8, int NG, bool SPLIT, int B>
+__global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
+                                                      const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
+                                                      uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t k,
+                                                      uint32_t log2S, const MvArgs a,
+                                                      const float *__restrict__ scale, float *__restrict__ y,
+                                                      float *__restrict__ partial) {
+  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
+  extern __shared__ uint32_t s_dyn[];
+  const uint32_t it = blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t off0 = items[2 * it], rows0 = items[2 * it + 1];
+  matvec_body<FP8, NG, SPLIT, B>(items, code, lut, x, n_groups, W, grid, blockIdx.x, k, log2S, a, scale, y, partial,
+                                 s_lut, s_dyn, off0, rows0);
+}
+
+// Several matrices of one work-item shape (elem, C, R, W; rows within one
+// workgroup) in one launch, each with its own activation and output: the
+// workgroups [begin[m], begin[m + 1]) run matrix m as the single-matrix kernel
+// runs it on a grid of that many workgroups, so each output is bit-equal to
+// the one nwc_matvec gives.
+//
+// What the first loads need comes in the leading scalar arguments, which
+// gfx950 preloads into scalar registers at wave launch: the count, W and
+// log2 S, the first workgroups of matrices 1 and 2, and the blob and
+// activation of matrices 0..2.  Everything else about a matrix is read from
+// its blob's header (one scalar load, issued beside the first item-table
+// read, so the first code rows wait no longer than in the single-matrix
+// kernel) or, for the output and the fp8 scales needed only at the end, from
+// the argument segment.  Matrices 3 and up take their blob and activation
+// from the argument segment too.
+constexpr int kGroupMax = NWC_GROUP_MAX;
+static_assert(NWC_GROUP_MAX < 16 && NWC_MAX_WAVES < 32, "group head packs the count in 4 bits and W in 5");
+constexpr uint32_t kGroupPreloaded = 3;
+struct GroupTail {
+  uint32_t begin[kGroupMax + 1];  // first workgroup of each matrix; begin[count] = grid
+  const uint8_t *blob[kGroupMax];
+  const uint16_t *x[kGroupMax];
+  const float *scale[kGroupMax];
+  float *y[kGroupMax];
+};
+
+template <bool FP8, int NG>
+__global__ __launch_bounds__(1024) void matvec_group_kernel(uint32_t head, uint32_t begins,
+                                                            const uint8_t *__restrict__ blob0,
+                                                            const uint8_t *__restrict__ blob1,
+                                                            const uint8_t *__restrict__ blob2,
+                                                            const uint16_t *__restrict__ x0,
+                                                            const uint16_t *__restrict__ x1,
+                                                            const uint16_t *__restrict__ x2, const GroupTail tail) {
+  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
+  extern __shared__ uint32_t s_dyn[];
+  // head: count | W << 4 | log2 S << 9 | from_tail << 12 | grid << 13;
+  // begins: first workgroup of matrix 1 | of matrix 2 << 16.  from_tail: the
+  // first workgroups do not fit those fields and come from the tail.
+  const uint32_t count = head & 15u, W = (head >> 4) & 31u, log2S = (head >> 9) & 7u;
+  const uint32_t wg = blockIdx.x, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t m, beg, end;
+  const uint8_t *blob;
+  const uint16_t *x;
+  if (count <= kGroupPreloaded && !((head >> 12) & 1u)) {
+    const uint32_t all = head >> 13;
+    const uint32_t b1 = count > 1 ? begins & 0xFFFFu : all, b2 = count > 2 ? begins >> 16 : all;
+    m = wg >= b2 ? 2u : wg >= b1 ? 1u : 0u;
+    beg = m == 0 ? 0u : m == 1 ? b1 : b2;
+    end = m == 0 ? b1 : m == 1 ? b2 : all;
+    blob = m == 0 ? blob0 : m == 1 ? blob1 : blob2;
+    x = m == 0 ? x0 : m == 1 ? x1 : x2;
+  } else {
+    m = 0;
+    for (uint32_t i = 1; i < count; ++i)
+      if (wg >= tail.begin[i]) m = i;
+    beg = tail.begin[m];
+    end = tail.begin[m + 1];
+    blob = tail.blob[m];
+    x = tail.x[m];
+  }
+  // The first item-table entry and the header fields, read before anything
+  // else (scalar loads: before the decode table's copy, which the compiler
+  // would count as a write that could alias them); the body issues the copy
+  // and then waits for all of them at once.  The item table and the decode
+  // table sit at fixed offsets in the blob.
+  const uint32_t *items = (const uint32_t *)(blob + NWC_HEADER_BYTES + NWC_LUT_BYTES);
+  const uint32_t it = (wg - beg) * W + wave;
+  const uint32_t off0 = items[2 * it], rows0 = items[2 * it + 1];
+  // Header fields as 32-bit words (nwc_header_t: n at word 4, k at 6, R at 9,
+  // row groups at 12, max_rows at 14, off_mant at 22-23, off_code at 24-25,
+  // rank_to_sym at 32); n and k are below 2^31.
+  const uint32_t *hw = (const uint32_t *)blob;
+  const uint32_t n = hw[4], k = hw[6], R = hw[9], n_groups = hw[12], max_rows = hw[14];
+  const uint32_t om_lo = hw[22], om_hi = hw[23], oc_lo = hw[24], oc_hi = hw[25];
+  const uint32_t r2s_lo = hw[32], r2s_hi = hw[33];
+  const uint64_t off_mant = ((uint64_t)om_hi << 32) | om_lo, off_code = ((uint64_t)oc_hi << 32) | oc_lo;
+  const uint32_t grid = end - beg;
+  MvArgs a;
+  a.mant = blob + off_mant;
+  a.n = n;
+  a.R = R;
+  a.n_spans = 1;
+  a.region_words = (max_rows + NWC_GUARD_ROWS) * 64;
+  a.r2s_lo = r2s_lo;
+  a.r2s_hi = r2s_hi;
+  a.groups_cap = (n_groups + grid - 1) / grid;
+  a.ldx = 0;
+  a.ldy = 0;
+  matvec_body<FP8, NG, false, 1>(items, blob + off_code, blob + NWC_HEADER_BYTES, x, n_groups, W, grid, wg - beg, k,
+                                 log2S, a, tail.scale[m], tail.y[m], nullptr, s_lut, s_dyn, off0, rows0);
 }
 
 // y[row] = (scale[row] *) sum over column spans of the partials, 16 threads
@@ -1063,6 +1194,75 @@ void launch_matvec_c(const Geom &g, hipStream_t s, const void *d_x, const float 
   }
 }
 
+// One launch over several matrices of one work-item shape (elem, C, R, W, one
+// span per row).  The persistent grid of the single-matrix launch (k
+// workgroups per CU, up to 25 waves per CU) is dealt to the matrices in
+// proportion to their row groups, so every workgroup gets about the same
+// number of groups; workgroup order follows matrix order.  The LDS request is
+// the largest any member needs, padded as for one matrix.  The kernel derives
+// each matrix's row-sum slots per workgroup (ceil(groups / its workgroups))
+// the same way.
+template <bool FP8, int NG>
+void launch_group(const Geom *g, const nwc_matvec_desc *d, int count, hipStream_t s) {
+  const void *kernel = (const void *)matvec_group_kernel<FP8, NG>;
+  const size_t static_lds = NWC_LUT_BYTES + (FP8 ? NWC_FP8_ESC_ENTRIES * 4 : 0);
+  const uint32_t W = g[0].W, slot = W * g[0].R * 4;
+  const uint32_t cap_slots = std::max<uint32_t>(1, 8192 / slot);
+  uint64_t total_groups = 0;
+  size_t probe = 0;
+  for (int m = 0; m < count; ++m) {
+    total_groups += (uint64_t)g[m].n_rowgroups;
+    probe = std::max(probe, matvec_lds(g[m], std::min<uint32_t>(cap_slots, 4)));
+  }
+  const Residency res = resident_per_cu(kernel, W * 64, probe);
+  uint64_t want = total_groups;
+  if (res.per_cu > 0) want = std::min<uint64_t>(total_groups, (uint64_t)res.per_cu * res.cus);
+  GroupTail tail;
+  memset(&tail, 0, sizeof tail);
+  uint32_t grid = 0;
+  size_t need = 0;
+  for (int m = 0; m < count; ++m) {
+    const uint32_t ng = g[m].n_rowgroups;
+    uint32_t gm = (uint32_t)std::max<uint64_t>(1, (want * ng + total_groups / 2) / std::max<uint64_t>(1, total_groups));
+    gm = std::min(gm, ng);
+    if ((ng + gm - 1) / gm > cap_slots) gm = (ng + cap_slots - 1) / cap_slots;
+    tail.begin[m] = grid;
+    tail.blob[m] = g[m].blob;
+    tail.x[m] = (const uint16_t *)d[m].d_x;
+    tail.scale[m] = d[m].d_scale;
+    tail.y[m] = d[m].d_y;
+    grid += gm;
+    need = std::max(need, matvec_lds(g[m], (ng + gm - 1) / gm));
+  }
+  tail.begin[count] = grid;
+  size_t lds = need;
+  if (res.per_cu > 0 && total_groups > (uint64_t)res.cus) {
+    const size_t per_group = ((res.lds_per_cu / (size_t)res.per_cu) & ~(size_t)1023) - 1024;
+    size_t share = per_group > static_lds ? per_group - static_lds : 0;
+    if (res.lds_per_group > static_lds) share = std::min(share, res.lds_per_group - static_lds);
+    lds = std::max(lds, share);
+  }
+  // Grid and first workgroups beyond the packed fields: the kernel reads them from the tail.
+  const bool wide = grid >= (1u << 19) || (count > 1 && tail.begin[1] > 0xFFFFu) || (count > 2 && tail.begin[2] > 0xFFFFu);
+  const uint32_t head = (uint32_t)count | (W << 4) | (g[0].log2S << 9) | (wide ? 1u << 12 : 0u) |
+                        (wide ? 0u : grid << 13);
+  const uint32_t begins = wide ? 0u : (count > 1 ? tail.begin[1] : 0u) | ((count > 2 ? tail.begin[2] : 0u) << 16);
+  const uint8_t *b[3] = {tail.blob[0], count > 1 ? tail.blob[1] : tail.blob[0], count > 2 ? tail.blob[2] : tail.blob[0]};
+  const uint16_t *xx[3] = {tail.x[0], count > 1 ? tail.x[1] : tail.x[0], count > 2 ? tail.x[2] : tail.x[0]};
+  hipLaunchKernelGGL((matvec_group_kernel<FP8, NG>), dim3(grid), dim3(W * 64), lds, s, head, begins, b[0], b[1], b[2],
+                     xx[0], xx[1], xx[2], tail);
+}
+
+template <bool FP8>
+void launch_group_c(const Geom *g, const nwc_matvec_desc *d, int count, hipStream_t s) {
+  switch (g[0].C) {
+    case 16: launch_group<FP8, 1>(g, d, count, s); break;
+    case 32: launch_group<FP8, 2>(g, d, count, s); break;
+    case 48: launch_group<FP8, 3>(g, d, count, s); break;
+    default: launch_group<FP8, 4>(g, d, count, s); break;
+  }
+}
+
 // B = 2 or 4 activation rows of a BF16 blob with one span per row and 16 or
 // 32 columns per lane (wider items would not keep B rows of activations in
 // registers).
@@ -1174,6 +1374,47 @@ int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const fl
     launch_matvec_c<true>(g, s, d_x, d_scale, d_y, partial);
   else
     launch_matvec_c<false>(g, s, d_x, d_scale, d_y, partial);
+  return launched();
+}
+
+int nwc_matvec_group(const nwc_matvec_desc *mats, int count, void *stream) {
+  if (count < 0 || count > NWC_GROUP_MAX) return NWC_ERR_SHAPE;
+  if (count == 0) return NWC_OK;
+  if (!mats) return NWC_ERR_ARG;
+  // Every member checked before anything is enqueued.
+  nwc_header_t h[NWC_GROUP_MAX];
+  Geom g[NWC_GROUP_MAX];
+  for (int m = 0; m < count; ++m) {
+    const nwc_matvec_desc &d = mats[m];
+    int st = read_header(d.header, h[m]);
+    if (st != NWC_OK) return st;
+    if (!d.d_blob || !d.d_x || !d.d_y || !aligned(d.d_blob, 16) || !aligned(d.d_x, 16) || !aligned(d.d_y, 4))
+      return NWC_ERR_ARG;
+    const bool fp8 = h[m].elem == NWC_FP8_E4M3;
+    if (fp8 != (d.d_scale != nullptr) || (d.d_scale && !aligned(d.d_scale, 4))) return NWC_ERR_ARG;
+    if (h[m].n_spans != 1) return NWC_ERR_UNSUPPORTED;
+    g[m] = make_geom(h[m], d.d_blob);
+  }
+  // One launch per work-item shape, members in their order of appearance.
+  hipStream_t s = (hipStream_t)stream;
+  bool done[NWC_GROUP_MAX] = {};
+  for (int m = 0; m < count; ++m) {
+    if (done[m]) continue;
+    Geom gs[NWC_GROUP_MAX];
+    nwc_matvec_desc ds[NWC_GROUP_MAX];
+    int c = 0;
+    for (int j = m; j < count; ++j) {
+      if (done[j] || h[j].elem != h[m].elem || g[j].C != g[m].C || g[j].R != g[m].R || g[j].W != g[m].W) continue;
+      done[j] = true;
+      gs[c] = g[j];
+      ds[c] = mats[j];
+      ++c;
+    }
+    if (h[m].elem == NWC_FP8_E4M3)
+      launch_group_c<true>(gs, ds, c, s);
+    else
+      launch_group_c<false>(gs, ds, c, s);
+  }
   return launched();
 }
 

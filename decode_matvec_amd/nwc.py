@@ -19,12 +19,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnwc.so")
 NWC_BF16 = 0
 NWC_FP8_E4M3 = 1
 HEADER_BYTES = 256
+GROUP_MAX = 12
 
 STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPACITY",
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
 EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info", "nwc_blob_check",
-           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
+           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_group", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
            "nwc_bf16_gemv")
 
 
@@ -42,6 +43,12 @@ class NWCInfo(ctypes.Structure):
                 ("coded_bits", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
                 ("code_bytes", ctypes.c_uint64), ("mant_bytes", ctypes.c_uint64),
                 ("table_bytes", ctypes.c_uint64), ("rank_to_sym", ctypes.c_uint8 * 128)]
+
+
+class MatvecDesc(ctypes.Structure):
+    """One member of nwc_matvec_group: the arguments of nwc_matvec without the workspace."""
+    _fields_ = [("header", ctypes.c_void_p), ("d_blob", ctypes.c_void_p), ("d_x", ctypes.c_void_p),
+                ("d_scale", ctypes.c_void_p), ("d_y", ctypes.c_void_p)]
 
 
 def _load():
@@ -64,6 +71,7 @@ def _load():
         "nwc_blob_check": ([vp, i64], ci),
         "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
         "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
+        "nwc_matvec_group": ([ctypes.POINTER(MatvecDesc), ci, vp], ci),
         "nwc_matvec_batch": ([vp, vp, vp, i64, i64, vp, vp, i64, vp, i64, vp], ci),
         "nwc_dequant": ([vp, vp, vp, i64, vp], ci),
         "nwc_gather": ([vp, vp, vp, i64, vp, vp], ci),
@@ -187,6 +195,26 @@ def matvec(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -
         _need("nwc_matvec", "scale", scale, n, 4, floating=True)
     _check("nwc_matvec", lib.nwc_matvec(_host_ptr(header), _dev(d_blob), _dev(x), _dev(scale), _dev(y), _dev(ws),
                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def matvec_group(mats, xs, ys, scales=None, stream=None) -> None:
+    """y_m = W_m x_m for every DeviceMatrix in ``mats`` in one launch per work-item shape (nwc_matvec_group).
+
+    xs / ys / scales: one device tensor per matrix (scales: None, or a list with fp32 scales for fp8 members)."""
+    count = len(mats)
+    if len(xs) != count or len(ys) != count or (scales is not None and len(scales) != count):
+        raise ValueError("nwc_matvec_group: one activation, output (and scale) per matrix")
+    if count > GROUP_MAX:
+        raise ValueError(f"nwc_matvec_group: at most {GROUP_MAX} matrices")
+    descs = (MatvecDesc * max(1, count))()
+    for i, dm in enumerate(mats):
+        sc = None if scales is None else scales[i]
+        _need("nwc_matvec_group", f"x[{i}]", xs[i], dm.k, 2)
+        _need("nwc_matvec_group", f"y[{i}]", ys[i], dm.n, 4, floating=True)
+        if dm.elem == NWC_FP8_E4M3:
+            _need("nwc_matvec_group", f"scale[{i}]", sc, dm.n, 4, floating=True)
+        descs[i] = MatvecDesc(_host_ptr(dm.header), _dev(dm.d_blob), _dev(xs[i]), _dev(sc), _dev(ys[i]))
+    _check("nwc_matvec_group", lib.nwc_matvec_group(descs, count, _stream(stream)))
 
 
 def matvec_batch(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -> None:

@@ -134,6 +134,33 @@ int nwc_workspace_size(const void *header, int64_t *bytes);
 int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const float *d_scale,
                float *d_y, void *d_ws, int64_t ws_bytes, void *stream);
 
+/* Several fused decode + matvec products in one launch: y_m = W_m x_m (times
+ * the fp8 row scales) for m < count, each matrix with its own activation and
+ * output.  This is the library's form of the pages' projection fusion ("Install"
+ * usage and "Run a model" on the PyPI page: projections that read the same
+ * input, such as q, k and v, or gate and up, run together): the matrices stay
+ * separately encoded, each with its own rank table, and share one kernel
+ * launch -- pass the same d_x for projections of one input.
+ *   mats     host array of count descriptors, each as the arguments of
+ *            nwc_matvec (host header copy, device blob, activation, fp8 scales
+ *            or NULL, output); 1 <= count <= NWC_GROUP_MAX (0 does nothing).
+ * Matrices of one work-item shape (element type, columns per lane, rows per
+ * wave, waves per workgroup) share a launch; a group of several shapes is one
+ * launch per shape, in order of first appearance.  Every output is bit-equal
+ * to nwc_matvec on the same matrix and activation.  Matrices whose rows span
+ * several workgroups (n_spans > 1) need a workspace and are refused
+ * (NWC_ERR_UNSUPPORTED).  Outputs must not overlap each other or any input.
+ * Every descriptor is checked before anything is enqueued. */
+#define NWC_GROUP_MAX 12
+typedef struct nwc_matvec_desc {
+  const void *header;
+  const void *d_blob;
+  const void *d_x;
+  const float *d_scale;
+  float *d_y;
+} nwc_matvec_desc;
+int nwc_matvec_group(const nwc_matvec_desc *mats, int count, void *stream);
+
 /* Fused decode + matvec for a small batch of activation rows (the pages'
  * batch-1 "token path" widened to a few tokens; "Fused kernel" and
  * "Limitations" describe batch 1 and the prefill route, a batch of several

@@ -339,3 +339,34 @@ def test_binding_checks_tensor_arguments_on_the_host():
     h8 = nwc.encode(q, elem=1)[:256].copy()
     with pytest.raises(ValueError):   # fp8 needs n fp32 scales
         nwc.matvec(h8, blob, ok_x, ok_y, scale=_FakeDev(69, 4, True))
+
+
+def test_matvec_group_rejects_bad_arguments_before_any_gpu_call():
+    L = nwc.lib
+    fake = 1 << 20  # aligned, never dereferenced: every call below fails its host-side checks first
+    w = S.normal_bf16(5, (70, 100), 0.02)
+    hdr = nwc.encode(w)[:256].copy()
+    _, two = _two_span()
+    hdr2 = two[:256].copy()
+
+    def descs(*rows):
+        arr = (nwc.MatvecDesc * max(1, len(rows)))()
+        for i, r in enumerate(rows):
+            arr[i] = nwc.MatvecDesc(*r)
+        return arr
+
+    ok = (hdr.ctypes.data, fake, fake, None, fake)
+    assert L.nwc_matvec_group(descs(ok), 0, None) == 0                       # nothing to do
+    assert L.nwc_matvec_group(descs(ok), -1, None) == -2
+    assert L.nwc_matvec_group(descs(*[ok] * 13), 13, None) == -2             # more than NWC_GROUP_MAX
+    assert L.nwc_matvec_group(None, 2, None) == -1
+    assert L.nwc_matvec_group(descs(ok, (hdr.ctypes.data, fake, fake + 4, None, fake)), 2, None) == -1  # x misaligned
+    assert L.nwc_matvec_group(descs(ok, (hdr.ctypes.data, fake, fake, fake, fake)), 2, None) == -1      # BF16 + scale
+    assert L.nwc_matvec_group(descs(ok, (None, fake, fake, None, fake)), 2, None) == -1
+    bad = hdr.copy()
+    bad[4] = 9
+    assert L.nwc_matvec_group(descs(ok, (bad.ctypes.data, fake, fake, None, fake)), 2, None) == -4
+    assert L.nwc_matvec_group(descs(ok, (hdr2.ctypes.data, fake, fake, None, fake)), 2, None) == -6     # split rows
+    q, _ = S.fp8_quantize(w)
+    h8 = nwc.encode(q, elem=1)[:256].copy()
+    assert L.nwc_matvec_group(descs(ok, (h8.ctypes.data, fake, fake, None, fake)), 2, None) == -1       # fp8, no scale

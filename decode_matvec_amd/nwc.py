@@ -26,7 +26,7 @@ STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPA
 
 EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info", "nwc_blob_check",
            "nwc_workspace_size", "nwc_matvec", "nwc_matvec_group", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
-           "nwc_bf16_gemv")
+           "nwc_bf16_gemv", "nwc_bf16_gemv_group")
 
 
 class NWCError(RuntimeError):
@@ -49,6 +49,12 @@ class MatvecDesc(ctypes.Structure):
     """One member of nwc_matvec_group: the arguments of nwc_matvec without the workspace."""
     _fields_ = [("header", ctypes.c_void_p), ("d_blob", ctypes.c_void_p), ("d_x", ctypes.c_void_p),
                 ("d_scale", ctypes.c_void_p), ("d_y", ctypes.c_void_p)]
+
+
+class GemvDesc(ctypes.Structure):
+    """One member of nwc_bf16_gemv_group: the arguments of nwc_bf16_gemv."""
+    _fields_ = [("d_w", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("ldw", ctypes.c_int64),
+                ("d_x", ctypes.c_void_p), ("d_y", ctypes.c_void_p)]
 
 
 def _load():
@@ -77,6 +83,7 @@ def _load():
         "nwc_gather": ([vp, vp, vp, i64, vp, vp], ci),
         "nwc_stream_read": ([vp, i64, vp, vp], ci),
         "nwc_bf16_gemv": ([vp, i64, i64, i64, vp, vp, vp], ci),
+        "nwc_bf16_gemv_group": ([ctypes.POINTER(GemvDesc), ci, vp], ci),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -267,6 +274,22 @@ def bf16_gemv(w, x, y, stream=None, k=None) -> None:
     _need("nwc_bf16_gemv", "y", y, n, 4, floating=True)
     _check("nwc_bf16_gemv", lib.nwc_bf16_gemv(_dev(w), n, k, w.stride(0), _dev(x), _dev(y),
                                               _stream(stream)))
+
+
+def bf16_gemv_group(ws, xs, ys, stream=None) -> None:
+    """Several plain BF16 GEMVs y_m = W_m x_m in one launch (measurement baseline); w: [n, ldw] device tensors."""
+    count = len(ws)
+    if len(xs) != count or len(ys) != count or count > GROUP_MAX:
+        raise ValueError("nwc_bf16_gemv_group: one activation and output per matrix, at most GROUP_MAX matrices")
+    descs = (GemvDesc * max(1, count))()
+    for i, w in enumerate(ws):
+        if w.dim() != 2 or w.element_size() != 2 or not w.is_cuda or w.stride(1) != 1:
+            raise ValueError("nwc_bf16_gemv_group: w must be a 2-D device tensor of 2-byte elements")
+        n, k = w.shape
+        _need("nwc_bf16_gemv_group", f"x[{i}]", xs[i], k, 2)
+        _need("nwc_bf16_gemv_group", f"y[{i}]", ys[i], n, 4, floating=True)
+        descs[i] = GemvDesc(_dev(w), n, k, w.stride(0), _dev(xs[i]), _dev(ys[i]))
+    _check("nwc_bf16_gemv_group", lib.nwc_bf16_gemv_group(descs, count, _stream(stream)))
 
 
 def gather(header: np.ndarray, d_blob, ids, out, stream=None) -> None:

@@ -197,13 +197,26 @@ int nwc_gather(const void *header, const void *d_blob, const int64_t *d_ids, int
 int nwc_stream_read(const void *d_buf, int64_t bytes, uint32_t *d_sink, void *stream);
 
 /* Measurement helper, not part of the method: the uncompressed baseline, a
- * plain BF16 GEMV y = W x with fp32 accumulation and no decode.
+ * plain BF16 GEMV y = W x with fp32 accumulation and no decode (one wave per
+ * row streaming 16-byte chunks of the row and of x).
  *   d_w  device, n rows of BF16 patterns, row pitch ldw elements (ldw >= k,
  *        a multiple of 8), 16-byte aligned.
- *   d_x  device, k BF16 patterns, 16-byte aligned; 8 <= k <= 24576, k a
- *        multiple of 8.  d_y: device, n fp32 outputs, 4-byte aligned.
+ *   d_x  device, k BF16 patterns, 16-byte aligned; k >= 8, a multiple of 8.
+ *   d_y  device, n fp32 outputs, 4-byte aligned.
  * NWC_ERR_ARG for null or misaligned pointers, NWC_ERR_SHAPE otherwise. */
 int nwc_bf16_gemv(const void *d_w, int64_t n, int64_t k, int64_t ldw, const void *d_x, float *d_y, void *stream);
+
+/* Measurement helper: several plain BF16 GEMVs in one launch (the launch
+ * structure of nwc_matvec_group), each described as the arguments of
+ * nwc_bf16_gemv; 1 <= count <= NWC_GROUP_MAX (0 does nothing).  Every
+ * descriptor is checked before anything is enqueued. */
+typedef struct nwc_bf16_gemv_desc {
+  const void *d_w;
+  int64_t n, k, ldw;
+  const void *d_x;
+  float *d_y;
+} nwc_bf16_gemv_desc;
+int nwc_bf16_gemv_group(const nwc_bf16_gemv_desc *mats, int count, void *stream);
 
 #ifdef __cplusplus
 }

@@ -271,8 +271,27 @@ def test_bf16_gemv_rejects_bad_arguments_before_any_gpu_call():
     assert L.nwc_bf16_gemv(fake + 8, 4, 64, 64, fake, fake, None) == -1       # w not 16-byte aligned
     assert L.nwc_bf16_gemv(fake, 4, 60, 64, fake, fake, None) == -2           # k not a multiple of 8
     assert L.nwc_bf16_gemv(fake, 4, 64, 56, fake, fake, None) == -2           # ldw < k
-    assert L.nwc_bf16_gemv(fake, 4, 24576 + 8, 24584, fake, fake, None) == -2  # activations over the LDS limit
+    assert L.nwc_bf16_gemv(fake, 4, 64, 60, fake, fake, None) == -2           # ldw not a multiple of 8
     assert L.nwc_bf16_gemv(fake, 0, 64, 64, fake, fake, None) == -2
+
+
+def test_bf16_gemv_group_rejects_bad_arguments_before_any_gpu_call():
+    L = nwc.lib
+    fake = 1 << 20
+    ok = (fake, 4, 64, 64, fake, fake)
+
+    def descs(*rows):
+        arr = (nwc.GemvDesc * max(1, len(rows)))()
+        for i, r in enumerate(rows):
+            arr[i] = nwc.GemvDesc(*r)
+        return arr
+
+    assert L.nwc_bf16_gemv_group(descs(ok), 0, None) == 0
+    assert L.nwc_bf16_gemv_group(descs(*[ok] * 13), 13, None) == -2
+    assert L.nwc_bf16_gemv_group(None, 1, None) == -1
+    assert L.nwc_bf16_gemv_group(descs(ok, (fake + 8, 4, 64, 64, fake, fake)), 2, None) == -1
+    assert L.nwc_bf16_gemv_group(descs(ok, (fake, 4, 60, 64, fake, fake)), 2, None) == -2
+    assert L.nwc_bf16_gemv_group(descs(ok, (fake, 0, 64, 64, fake, fake)), 2, None) == -2
 
 
 def test_one_hip_runtime_whatever_the_import_order():

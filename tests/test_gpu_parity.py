@@ -455,3 +455,28 @@ def test_matvec_group_mixed_shapes_fp8_and_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert all(torch.equal(y, y1) for y, y1 in zip(ys, singles))
+
+
+def test_bf16_gemv_group_reference():
+    """The grouped plain BF16 GEMV baseline: every member within the bound of the oracle's float64 sum, and
+    bit-equal to the single-matrix baseline."""
+    shapes = [(4096, 2560, 2560), (1024, 2560, 2560), (1023, 2560, 2560), (7, 8, 16), (300, 9728, 9728),
+              (5, 24576 + 8, 24576 + 8)]
+    ws, xs, ys, ys1, refs = [], [], [], [], []
+    for i, (n, k, ld) in enumerate(shapes):
+        w = S.student_t_bf16(150 + i, (n, k))
+        x = S.activation_bf16(160 + i, k)
+        wp = np.zeros((n, ld), dtype=np.uint16)
+        wp[:, :k] = w
+        ws.append(dev16(wp)[:, :k] if ld != k else dev16(wp))
+        xs.append(dev16(x))
+        ys.append(torch.full((n,), float("nan"), dtype=torch.float32, device=DEV))
+        y1 = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+        nwc.bf16_gemv(dev16(wp), dev16(x), y1, k=k)
+        ys1.append(y1)
+        refs.append(O.matvec_bf16_ref(w, x))
+    nwc.bf16_gemv_group(ws, xs, ys)
+    torch.cuda.synchronize()
+    for y, y1, (y_ref, A) in zip(ys, ys1, refs):
+        check_tol(y.cpu().numpy().astype(np.float64), y_ref, A, "bf16 gemv group")
+        assert torch.equal(y, y1)

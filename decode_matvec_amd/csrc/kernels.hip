@@ -1348,6 +1348,32 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Scratch of nwc_matvec_noalloc: the fp32 span partials of matrices whose
+// rows span several workgroups, in a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// `nwc_scratch` only names the array; its device address, which differs per
+// GPU, comes from hipGetSymbolAddress, taken once per device with that device
+// current and kept in scratch_ptr[].
+__device__ __align__(256) float nwc_scratch[NWC_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this GPU's nwc_scratch (nullptr and NWC_ERR_HIP on failure).
+int scratch_for_current_device(float **out) {
+  static std::mutex mu;
+  static float *ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NWC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(nwc_scratch)) != hipSuccess || !p) return NWC_ERR_HIP;
+    ptr[dev] = (float *)p;
+  }
+  *out = ptr[dev];
+  return NWC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1368,6 +1394,28 @@ int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const fl
     if (ws_bytes < need) return NWC_ERR_CAPACITY;
     partial = (float *)d_ws;
   }
+  const Geom g = make_geom(h, d_blob);
+  hipStream_t s = (hipStream_t)stream;
+  if (fp8)
+    launch_matvec_c<true>(g, s, d_x, d_scale, d_y, partial);
+  else
+    launch_matvec_c<false>(g, s, d_x, d_scale, d_y, partial);
+  return launched();
+}
+
+int nwc_matvec_noalloc(const void *header, const void *d_blob, const void *d_x, const float *d_scale, float *d_y,
+                       void *stream) {
+  nwc_header_t h;
+  int st = read_header(header, h);
+  if (st != NWC_OK) return st;
+  int64_t need = 0;
+  if ((st = nwc_workspace_size(header, &need)) != NWC_OK) return st;
+  if (need > (int64_t)NWC_NOALLOC_SCRATCH_BYTES) return NWC_ERR_CAPACITY;
+  if (!d_blob || !d_x || !d_y || !aligned(d_blob, 16) || !aligned(d_x, 16) || !aligned(d_y, 4)) return NWC_ERR_ARG;
+  const bool fp8 = h.elem == NWC_FP8_E4M3;
+  if (fp8 != (d_scale != nullptr) || (d_scale && !aligned(d_scale, 4))) return NWC_ERR_ARG;
+  float *partial = nullptr;
+  if (need > 0 && (st = scratch_for_current_device(&partial)) != NWC_OK) return st;
   const Geom g = make_geom(h, d_blob);
   hipStream_t s = (hipStream_t)stream;
   if (fp8)

@@ -25,7 +25,7 @@ STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPA
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
 EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info", "nwc_blob_check",
-           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_group", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
+           "nwc_workspace_size", "nwc_matvec", "nwc_matvec_noalloc", "nwc_matvec_group", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
            "nwc_bf16_gemv", "nwc_bf16_gemv_group")
 
 
@@ -77,6 +77,7 @@ def _load():
         "nwc_blob_check": ([vp, i64], ci),
         "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
         "nwc_matvec": ([vp, vp, vp, vp, vp, vp, i64, vp], ci),
+        "nwc_matvec_noalloc": ([vp, vp, vp, vp, vp, vp], ci),
         "nwc_matvec_group": ([ctypes.POINTER(MatvecDesc), ci, vp], ci),
         "nwc_matvec_batch": ([vp, vp, vp, i64, i64, vp, vp, i64, vp, i64, vp], ci),
         "nwc_dequant": ([vp, vp, vp, i64, vp], ci),
@@ -202,6 +203,20 @@ def matvec(header: np.ndarray, d_blob, x, y, ws=None, scale=None, stream=None) -
         _need("nwc_matvec", "scale", scale, n, 4, floating=True)
     _check("nwc_matvec", lib.nwc_matvec(_host_ptr(header), _dev(d_blob), _dev(x), _dev(scale), _dev(y), _dev(ws),
                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def matvec_noalloc(header: np.ndarray, d_blob, x, y, scale=None, stream=None) -> None:
+    """nwc_matvec without a workspace: split-row partials live in the library's static per-GPU scratch."""
+    n, k, elem = _shape(header)
+    _need("nwc_matvec_noalloc", "x", x, k, 2)
+    _need("nwc_matvec_noalloc", "y", y, n, 4, floating=True)
+    if elem == NWC_FP8_E4M3:
+        _need("nwc_matvec_noalloc", "scale", scale, n, 4, floating=True)
+    _check("nwc_matvec_noalloc", lib.nwc_matvec_noalloc(_host_ptr(header), _dev(d_blob), _dev(x), _dev(scale),
+                                                        _dev(y), _stream(stream)))
 
 
 def matvec_group(mats, xs, ys, scales=None, stream=None) -> None:

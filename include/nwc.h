@@ -134,6 +134,22 @@ int nwc_workspace_size(const void *header, int64_t *bytes);
 int nwc_matvec(const void *header, const void *d_blob, const void *d_x, const float *d_scale,
                float *d_y, void *d_ws, int64_t ws_bytes, void *stream);
 
+/* nwc_matvec for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and the same bits as nwc_matvec, with no workspace argument.
+ * Matrices whose rows span several workgroups (nwc_workspace_size > 0) keep
+ * their fp32 span partials in a static device array of the library,
+ * NWC_NOALLOC_SCRATCH_BYTES per GPU, held from the first call on a GPU until
+ * the process ends; a matrix needing more is refused (NWC_ERR_CAPACITY, with
+ * nothing enqueued).  Nothing is allocated and nothing needs clearing (every
+ * partial is written before it is read).  All calls on one GPU share its
+ * array: calls that may overlap in time on one GPU (different streams, or
+ * several threads) race on it and must be serialized by the caller; calls on
+ * one stream are ordered.  Other arguments and errors as nwc_matvec. */
+#define NWC_NOALLOC_SCRATCH_BYTES (4u << 20)
+int nwc_matvec_noalloc(const void *header, const void *d_blob, const void *d_x, const float *d_scale, float *d_y,
+                       void *stream);
+
 /* Several fused decode + matvec products in one launch: y_m = W_m x_m (times
  * the fp8 row scales) for m < count, each matrix with its own activation and
  * output.  This is the library's form of the pages' projection fusion ("Install"

@@ -389,3 +389,39 @@ def test_matvec_group_rejects_bad_arguments_before_any_gpu_call():
     q, _ = S.fp8_quantize(w)
     h8 = nwc.encode(q, elem=1)[:256].copy()
     assert L.nwc_matvec_group(descs(ok, (h8.ctypes.data, fake, fake, None, fake)), 2, None) == -1       # fp8, no scale
+
+
+def _grown_header(hdr, n):
+    """A valid header of the same geometry for n rows (dependent fields recomputed; never launched)."""
+    h = np.frombuffer(hdr.tobytes(), dtype=BL.HDR)[0].copy()
+    R, W, sp = int(h["rows_per_wave"]), int(h["waves_per_group"]), int(h["n_spans"])
+    h["n"] = n
+    h["n_rowgroups"] = (n + R - 1) // R
+    h["n_items"] = int(h["n_rowgroups"]) * sp * W
+    h["off_mant"] = int(h["off_items"]) + (int(h["n_items"]) * 8 + 255) // 256 * 256
+    h["mant_bytes"] = int(h["n_items"]) * 64 * int(h["cols_per_lane"])
+    h["off_code"] = int(h["off_mant"]) + int(h["mant_bytes"])
+    h["code_bytes"] = int(h["n_items"]) * 256
+    h["total_bytes"] = int(h["off_code"]) + int(h["code_bytes"])
+    return np.frombuffer(h.tobytes(), dtype=np.uint8).copy()
+
+
+def test_matvec_noalloc_rejects_bad_arguments_before_any_gpu_call():
+    L = nwc.lib
+    fake = 1 << 20
+    _, blob = _two_span()
+    hdr = blob[:256].copy()
+    assert nwc.workspace_size(hdr) <= nwc.NOALLOC_SCRATCH_BYTES
+    assert L.nwc_matvec_noalloc(None, fake, fake, None, fake, None) == -1
+    assert L.nwc_matvec_noalloc(hdr.ctypes.data, 0, fake, None, fake, None) == -1
+    assert L.nwc_matvec_noalloc(hdr.ctypes.data, fake, fake + 4, None, fake, None) == -1
+    assert L.nwc_matvec_noalloc(hdr.ctypes.data, fake, fake, fake, fake, None) == -1     # BF16 with a scale
+    bad = hdr.copy()
+    bad[4] = 9
+    assert L.nwc_matvec_noalloc(bad.ctypes.data, fake, fake, None, fake, None) == -4
+    # Partials beyond the static scratch: refused with a capacity error, nothing enqueued.
+    big = _grown_header(hdr, 300000)
+    assert nwc.workspace_size(big) > nwc.NOALLOC_SCRATCH_BYTES
+    assert L.nwc_matvec_noalloc(big.ctypes.data, fake, fake, None, fake, None) == -3
+    fits = _grown_header(hdr, 200000)
+    assert nwc.workspace_size(fits) <= nwc.NOALLOC_SCRATCH_BYTES

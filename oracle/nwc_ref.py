@@ -21,6 +21,8 @@ __all__ = [
     "kraft_sum_bf16", "parse_one_bf16", "bf16_value", "matvec_bf16_ref",
     "split_fp8", "codeword_fp8", "code_length_fp8", "encode_fp8", "decode_fp8",
     "fp8_e4m3fn_value", "matvec_fp8_ref", "gather_bf16_ref", "coded_bits_closed_form_fp8",
+    "HUFF_MAX_LEN", "huffman_lengths_limited", "canonical_codes", "kraft_sum", "codeword_huffman",
+    "encode_fp8_huffman", "decode_fp8_huffman",
 ]
 
 # Escape threshold.  The pages say only "escape for rare values" (PyPI page,
@@ -354,3 +356,124 @@ def matvec_fp8_ref(q_u8, scale_f32, x_u16):
     x = bf16_value(x_u16)
     s = np.asarray(scale_f32, dtype=np.float32).astype(np.float64)
     return s * (q @ x), np.abs(s) * (np.abs(q) @ np.abs(x))
+
+
+# ---------------------------------------------------------------------------
+# fp8 coder variant: a length-limited canonical Huffman code over whole fp8
+# bytes.  The model card "Qwen3-4B-NWC-fp8" (summary) codes the fp8 bytes
+# whole; the third-party article (section on the limits of lossless weight
+# compression) puts the current coder's saving well below the ideal.  Readings
+# taken: every byte that occurs gets an optimal prefix code with no codeword
+# longer than max_len bits (found by package-merge); canonical codewords
+# (symbols in order of (length, byte); first all zeros; each next = previous
+# + 1, shifted left by the growth in length); codewords written most
+# significant bit first.  max_len = 12 is the library's decode-table peek.
+# ---------------------------------------------------------------------------
+HUFF_MAX_LEN = 12
+
+
+def huffman_lengths_limited(counts, max_len: int = HUFF_MAX_LEN) -> list:
+    """Optimal code lengths (at most max_len bits) of the symbols with a nonzero count, by package-merge.
+
+    Leaves are the symbols, weighted by count.  Starting from the sorted
+    leaves, max_len - 1 times: pair neighbours into packages (weight sum) and
+    merge the packages with the leaves in weight order.  The first 2n - 2 items
+    of the final list are the chosen ones; a symbol's length is the number of
+    chosen items it appears in.  A lone symbol gets length 1."""
+    counts = [int(c) for c in counts]
+    syms = [s for s in range(len(counts)) if counts[s] > 0]
+    lengths = [0] * len(counts)
+    if not syms:
+        return lengths
+    if len(syms) == 1:
+        lengths[syms[0]] = 1
+        return lengths
+    if (1 << max_len) < len(syms):
+        raise ValueError("too many symbols for the length limit")
+    leaves = sorted(((counts[s], (s,)) for s in syms), key=lambda t: (t[0], t[1]))
+    cur = list(leaves)
+    for _ in range(max_len - 1):
+        packages = [(cur[i][0] + cur[i + 1][0], cur[i][1] + cur[i + 1][1]) for i in range(0, len(cur) - 1, 2)]
+        cur = sorted(leaves + packages, key=lambda t: t[0])  # stable: leaves before equal packages
+    for _, members in cur[:2 * len(syms) - 2]:
+        for s in members:
+            lengths[s] += 1
+    return lengths
+
+
+def canonical_codes(lengths) -> dict:
+    """{symbol: (codeword value, length)} of the canonical code with these lengths (0 = no codeword)."""
+    order = sorted((l, s) for s, l in enumerate(lengths) if l > 0)
+    codes, code, prev = {}, 0, None
+    for l, s in order:
+        if prev is not None:
+            code = (code + 1) << (l - prev)
+        codes[s] = (code, l)
+        prev = l
+    return codes
+
+
+def kraft_sum(lengths):
+    from fractions import Fraction
+    return sum(Fraction(1, 2 ** l) for l in lengths if l > 0)
+
+
+def codeword_huffman(code: int, length: int) -> list:
+    """Bits of a codeword in stream order (most significant bit first)."""
+    return [(code >> (length - 1 - i)) & 1 for i in range(length)]
+
+
+def encode_fp8_huffman(q_u8, max_len: int = HUFF_MAX_LEN) -> dict:
+    """Per-row streams of the fp8 bytes under the matrix's length-limited canonical Huffman code."""
+    q = np.ascontiguousarray(q_u8, dtype=np.uint8)
+    n, k = q.shape
+    counts = np.bincount(q.reshape(-1).astype(np.int64), minlength=256)
+    lengths = huffman_lengths_limited(counts, max_len)
+    codes = canonical_codes(lengths)
+    val = np.zeros(256, dtype=np.uint32)
+    ln = np.zeros(256, dtype=np.int64)
+    for s, (c, l) in codes.items():
+        bits = codeword_huffman(c, l)
+        val[s] = sum(b << i for i, b in enumerate(bits))
+        ln[s] = l
+    bits, row_off, row_bits = _pack_rows(q.astype(np.int64), val, ln, n, k)
+    return dict(kind="fp8_huffman", n=n, k=k, counts=counts, lengths=np.array(lengths), max_len=max_len,
+                bits=bits, row_off=row_off, row_bits=row_bits, coded_bits=int(row_bits.sum()))
+
+
+def decode_fp8_huffman(enc: dict) -> np.ndarray:
+    """Canonical decode, vectorised across rows: read bits one by one, MSB first, until the value read is a
+    codeword of the current length (codewords of length l are the values first[l] .. first[l] + count[l] - 1)."""
+    n, k, L = enc["n"], enc["k"], enc["max_len"]
+    lengths = [int(v) for v in enc["lengths"]]
+    codes = canonical_codes(lengths)
+    first = np.zeros(L + 2, dtype=np.int64)
+    num = np.zeros(L + 2, dtype=np.int64)
+    sym_at = {}
+    for s, (c, l) in codes.items():
+        num[l] += 1
+        sym_at[(l, c)] = s
+    for l in range(1, L + 1):
+        cs = [c for (ll, c) in sym_at if ll == l]
+        first[l] = min(cs) if cs else 0
+    table = np.full((L + 1, 1 << L), -1, dtype=np.int64)
+    for (l, c), s in sym_at.items():
+        table[l, c] = s
+    bits = enc["bits"]
+    pos = enc["row_off"].copy()
+    out = np.empty((n, k), dtype=np.uint8)
+    for j in range(k):
+        code = np.zeros(n, dtype=np.int64)
+        sym = np.full(n, -1, dtype=np.int64)
+        used = np.zeros(n, dtype=np.int64)
+        for l in range(1, L + 1):
+            live = sym < 0
+            code = np.where(live, (code << 1) | bits[pos + l - 1], code)
+            hit = live & (table[l, np.minimum(code, (1 << L) - 1)] >= 0) & (code < (1 << l))
+            sym = np.where(hit, table[l, np.minimum(code, (1 << L) - 1)], sym)
+            used = np.where(hit, l, used)
+        assert (sym >= 0).all(), "stream does not parse"
+        pos += used
+        out[:, j] = sym.astype(np.uint8)
+    assert np.array_equal(pos, enc["row_off"] + enc["row_bits"])
+    return out

@@ -480,3 +480,32 @@ def test_bf16_gemv_group_reference():
     for y, y1, (y_ref, A) in zip(ys, ys1, refs):
         check_tol(y.cpu().numpy().astype(np.float64), y_ref, A, "bf16 gemv group")
         assert torch.equal(y, y1)
+
+
+# ----------------------------------------------------------------- blob files on the device
+def test_blob_file_round_trip_runs_every_kernel(tmp_path):
+    # Encode, save to a blob file, load it back (host check of every blob) and
+    # run the kernels on the loaded blobs: dequant and gather bit-exact and the
+    # matvec (fp8 with the scales stored beside it) in tolerance against the
+    # oracle -- no BF16 original is needed after the save.
+    from decode_matvec_amd import store
+    w = S.inject_rare(S.normal_bf16(171, (1000, 3001), 0.02), 172)
+    q, sc = S.fp8_quantize(S.normal_bf16(173, (300, 2560), 0.02))
+    path = str(tmp_path / "layer.safetensors")
+    store.save(path, {"w": nwc.encode(w), "q": nwc.encode(q, elem=nwc.NWC_FP8_E4M3)}, {"q_scale": sc})
+    blobs, arrays = store.load(path)
+    dm = nwc.DeviceMatrix(blobs["w"], DEV)
+    assert np.array_equal(dequant_host(dm), w)
+    x = S.activation_bf16(174, 3001)
+    y_ref, A = O.matvec_bf16_ref(w, x)
+    check_tol(run_matvec(dm, x), y_ref, A, "loaded bf16 blob")
+    ids = np.array([0, 999, 5, 5, 512], dtype=np.int64)
+    out = torch.full((len(ids), 3001), -1, dtype=torch.int16, device=DEV)
+    dm.gather(torch.from_numpy(ids).to(DEV), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), w[ids])
+    d8 = nwc.DeviceMatrix(blobs["q"], DEV)
+    assert np.array_equal(dequant_host(d8), q)
+    x8 = S.activation_bf16(175, 2560)
+    y_ref, A = O.matvec_fp8_ref(q, arrays["q_scale"], x8)
+    check_tol(run_matvec(d8, x8, scale=arrays["q_scale"]), y_ref, A, "loaded fp8 blob")

@@ -364,3 +364,100 @@ def test_fp8_coded_bits_against_byte_entropy():
     print(f"fp8 1024x1024: H(byte) {h:.4f} bits, coded {per:.4f} bits ({per / h - 1:+.2%}), "
           f"{per / 8:.4f} of the fp8 bytes", flush=True)
     assert h <= per <= h + 1
+
+
+# --------------------------------------------------------------- fp8 coder variant (length-limited Huffman)
+GOLDEN_HUFF = os.path.join(os.path.dirname(__file__), "golden", "fp8_huffman_codes.txt")
+
+
+def load_huffman_golden():
+    ex = {"lengths": {}, "total": {}, "codes": {}, "row": {}, "rowbits": {}}
+    for line in open(GOLDEN_HUFF):
+        p = line.split()
+        if not p or p[0].startswith("#"):
+            continue
+        if p[0] == "counts":
+            ex["counts"] = {int(a, 16): int(b) for a, b in (t.split(":") for t in p[2:])}
+        elif p[0] == "lengths":
+            ex["lengths"][int(p[2])] = {int(a, 16): int(b) for a, b in (t.split(":") for t in p[3:])}
+        elif p[0] == "total":
+            ex["total"][int(p[2])] = int(p[3])
+        elif p[0] == "codes":
+            ex["codes"][int(p[2])] = {int(a, 16): [int(c) for c in b] for a, b in (t.split(":") for t in p[3:])}
+        elif p[0] == "row":
+            ex["row"][int(p[2])] = [int(v, 16) for v in p[3:]]
+        elif p[0] == "rowbits":
+            ex["rowbits"][int(p[2])] = [int(c) for c in p[3]]
+    return ex
+
+
+def test_huffman_golden_example():
+    ex = load_huffman_golden()
+    counts = np.zeros(256, np.int64)
+    for s, c in ex["counts"].items():
+        counts[s] = c
+    for L, total in ex["total"].items():
+        lengths = O.huffman_lengths_limited(counts, L)
+        assert sum(int(counts[s]) * lengths[s] for s in range(256)) == total
+        assert max(lengths) <= L and O.kraft_sum(lengths) <= 1
+        if L in (3, 4):   # the optimal lengths are unique there (derivation in the file)
+            assert {s: lengths[s] for s in ex["lengths"][L]} == ex["lengths"][L]
+    for L, words in ex["codes"].items():
+        codes = O.canonical_codes(O.huffman_lengths_limited(counts, L))
+        assert {s: O.codeword_huffman(*codes[s]) for s in words} == words
+    row = np.array([ex["row"][4]], dtype=np.uint8)
+    enc = O.encode_fp8_huffman(row, max_len=4)
+    assert list(enc["bits"][:enc["row_bits"][0]]) == ex["rowbits"][4]
+    assert enc["coded_bits"] == ex["total"][4]
+    assert np.array_equal(O.decode_fp8_huffman(enc), row)
+
+
+def test_huffman_lengths_optimal_bruteforce():
+    # Every length vector of 1..L bits per symbol with Kraft sum <= 1 is a
+    # prefix code (Kraft-McMillan); the package-merge lengths must reach the
+    # smallest total among all of them.
+    rng = np.random.default_rng(17)
+    for trial in range(40):
+        a = int(rng.integers(2, 7))
+        counts = rng.integers(1, 60, size=a)
+        for L in (max(1, int(np.ceil(np.log2(a)))), 3, 4, 6):
+            if (1 << L) < a:
+                continue
+            got = O.huffman_lengths_limited(counts, L)
+            best = min(sum(int(c) * l for c, l in zip(counts, ls))
+                       for ls in itertools.product(range(1, L + 1), repeat=a)
+                       if sum(Fraction(1, 2 ** l) for l in ls) <= 1)
+            assert sum(int(c) * l for c, l in zip(counts, got)) == best, (counts, L, got)
+
+
+def test_huffman_codes_prefix_free_and_complete():
+    q, _ = S.fp8_quantize(S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"]))
+    counts = np.bincount(q.reshape(-1), minlength=256)
+    lengths = O.huffman_lengths_limited(counts)
+    assert max(lengths) <= O.HUFF_MAX_LEN
+    assert O.kraft_sum(lengths) == 1     # an optimal code with two or more symbols is complete
+    words = [tuple(O.codeword_huffman(*cl)) for cl in O.canonical_codes(lengths).values()]
+    for a in words:
+        for b in words:
+            if a is not b:
+                assert a != b[:len(a)], "codeword is a prefix of another"
+
+
+def test_huffman_fp8_size_against_entropy_and_the_unary_code():
+    q, _ = S.fp8_quantize(S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"]))
+    h = O.byte_entropy(q)
+    huff = O.encode_fp8_huffman(q)
+    unary = O.encode_fp8(q)
+    per = huff["coded_bits"] / q.size
+    print(f"fp8 1024x1024: H(byte) {h:.4f}, Huffman (<= 12 bits) {per:.4f} ({per / 8:.4f} of the bytes), "
+          f"unary-rank code {unary['coded_bits'] / q.size:.4f}", flush=True)
+    assert h <= per <= h + 1
+    assert huff["coded_bits"] < unary["coded_bits"]
+    assert np.array_equal(O.decode_fp8_huffman(huff), q)
+
+
+def test_huffman_round_trips():
+    for q in (S.all_bytes_fp8(3), np.full((3, 7), 0x38, np.uint8),
+              S.fp8_quantize(S.odd_shape_matrix(1, "t3")[0])[0]):
+        enc = O.encode_fp8_huffman(q)
+        assert np.array_equal(O.decode_fp8_huffman(enc), q)

@@ -375,23 +375,28 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
     fp8 = {}
     for tag, (fn_, fk, seeds) in {"single_1024": (1024, 1024, [C.SINGLE["w_seed"]]),
                                    "gate_9728x2560": (9728, 2560, list(range(600000, 600012)))}.items():
-        dms, scs = [], []
+        qs = []
         for sd in seeds:
             if fn_ == 1024:
                 wf = S.normal_bf16(sd, (fn_, fk), C.SINGLE["sigma"])
             else:
                 wf = S.blocked_normal_bf16(sd, (fn_, fk), np.float32(C.sigma_for(fk)))
-            q, sc = S.fp8_quantize(wf)
-            dms.append(nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), dev))
-            scs.append(torch.from_numpy(sc).to(dev))
+            qs.append(S.fp8_quantize(wf))
         xf = torch.from_numpy(S.activation_bf16(C.SINGLE["x_seed"], fk).view(np.int16)).to(dev)
         yf = torch.empty(fn_, dtype=torch.float32, device=dev)
-        reps = max(1, 32 // len(dms))
-        msf = per_call_ms(lambda: [d.matvec(xf, yf, scale=sc) for d, sc in zip(dms, scs)], reps) / len(dms)
-        fa = dms[0].info["coded_bits"] / 8.0 + 2 * fk + 4 * fn_
-        fp8[tag] = {"us": round(msf * 1e3, 3), "compressed_GBps": round(fa / (msf * 1e-3) / 1e9, 1),
-                    "bits_per_weight_coded": round(dms[0].info["coded_bits"] / (fn_ * fk), 4),
-                    "rotation": len(dms)}
+        fp8[tag] = {}
+        # Both coders of the bytes: the unary rank code and the length-limited Huffman variant.
+        for cname, coder in (("unary", nwc.NWC_CODER_UNARY), ("huffman", nwc.NWC_CODER_HUFFMAN)):
+            dms = [nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=coder), dev) for q, _ in qs]
+            scs = [torch.from_numpy(sc).to(dev) for _, sc in qs]
+            reps = max(1, 32 // len(dms))
+            msf = per_call_ms(lambda: [d.matvec(xf, yf, scale=sc) for d, sc in zip(dms, scs)], reps) / len(dms)
+            fa = dms[0].info["coded_bits"] / 8.0 + 2 * fk + 4 * fn_
+            fp8[tag][cname] = {"us": round(msf * 1e3, 3), "compressed_GBps": round(fa / (msf * 1e-3) / 1e9, 1),
+                               "bits_per_weight_coded": round(dms[0].info["coded_bits"] / (fn_ * fk), 4),
+                               "bits_per_weight_blob": round(dms[0].nbytes * 8 / (fn_ * fk), 4),
+                               "rotation": len(dms)}
+            del dms
     out_j = {"metric": "tied embedding 151936x2560: lm_head GEMV, 4096-id gather, dequant; fp8 e4m3 variant",
              "value": round(algo / (ms_mv * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
              "warmup": args.warmup, "ms_per_step": round(ms_mv, 4), "higher_is_better": True, "scaling": "weak",

@@ -8,6 +8,7 @@
 // described in nwc_format.h.
 #include <algorithm>
 #include <climits>
+#include <utility>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -136,6 +137,93 @@ void build_lut_fp8(const uint8_t *rank_to_sym, uint32_t *lut) {
   }
 }
 
+// ------------------------------------------------------------ Huffman variant
+// Length-limited Huffman code over whole fp8 bytes (nwc_format.h, coder
+// variant).  Lengths by package-merge: the present symbols, sorted by count,
+// are the leaves; max_len - 1 times, neighbouring items are paired into
+// packages and the packages merged back with the leaves in count order; of the
+// final list the first 2n - 2 items are kept, and a symbol's length is the
+// number of kept items that contain it.  Optimal among prefix codes with no
+// codeword longer than max_len.  A lone symbol gets one bit.
+void huffman_lengths(const uint64_t *counts, int alphabet, int max_len, uint8_t *len) {
+  struct Item {
+    uint64_t w;
+    std::vector<uint16_t> syms;
+  };
+  std::vector<Item> leaves;
+  for (int s = 0; s < alphabet; ++s) {
+    len[s] = 0;
+    if (counts[s]) leaves.push_back({counts[s], {(uint16_t)s}});
+  }
+  if (leaves.empty()) return;
+  if (leaves.size() == 1) {
+    len[leaves[0].syms[0]] = 1;
+    return;
+  }
+  auto by_weight = [](const Item &a, const Item &b) { return a.w < b.w; };
+  std::stable_sort(leaves.begin(), leaves.end(), by_weight);
+  std::vector<Item> cur = leaves;
+  for (int level = 1; level < max_len; ++level) {
+    std::vector<Item> next = leaves;
+    for (size_t i = 0; i + 1 < cur.size(); i += 2) {
+      Item p{cur[i].w + cur[i + 1].w, cur[i].syms};
+      p.syms.insert(p.syms.end(), cur[i + 1].syms.begin(), cur[i + 1].syms.end());
+      next.push_back(std::move(p));
+    }
+    std::stable_sort(next.begin(), next.end(), by_weight);
+    cur = std::move(next);
+  }
+  for (size_t i = 0; i < 2 * leaves.size() - 2; ++i)
+    for (uint16_t s : cur[i].syms) len[s]++;
+}
+
+// Canonical codewords for the lengths: symbols in order of (length, value),
+// the first all zeros, each next the previous plus one shifted left by the
+// growth in length.  The table holds each codeword bit-reversed, so that the
+// stream (least significant bit first) carries it most significant bit first.
+void huffman_codes(const uint8_t *len, CodeTable &t) {
+  std::vector<std::pair<int, int>> order;
+  for (int b = 0; b < 256; ++b) {
+    t.val[b] = 0;
+    t.len[b] = len[b];
+    if (len[b]) order.push_back({len[b], b});
+  }
+  std::sort(order.begin(), order.end());
+  uint32_t code = 0;
+  for (size_t i = 0; i < order.size(); ++i) {
+    const int l = order[i].first, b = order[i].second;
+    if (i) code = (code + 1) << (l - order[i - 1].first);
+    uint32_t rev = 0;
+    for (int j = 0; j < l; ++j) rev |= ((code >> j) & 1u) << (l - 1 - j);
+    t.val[b] = rev;
+  }
+}
+
+// Decode table of the Huffman variant: every peek whose first len[b] bits are
+// byte b's codeword decodes to b (its BF16 value, the byte, the length).  Peeks
+// that start no codeword (only when the code is incomplete, e.g. a single
+// symbol) are flagged; a valid stream never meets one.
+void build_lut_fp8_huffman(const uint8_t *len, uint32_t *lut) {
+  CodeTable t;
+  huffman_codes(len, t);
+  for (uint32_t p = 0; p < NWC_LUT_ENTRIES; ++p) lut[p] = 0x80000000u;
+  for (int b = 0; b < 256; ++b) {
+    if (!len[b]) continue;
+    for (uint32_t p = t.val[b]; p < NWC_LUT_ENTRIES; p += 1u << len[b])
+      lut[p] = fp8_to_bf16((uint32_t)b) | ((uint32_t)b << 16) | ((uint32_t)len[b] << 24);
+  }
+}
+
+void pack_nibbles(const uint8_t *len, uint8_t *out128) {
+  for (int i = 0; i < 128; ++i) out128[i] = (uint8_t)((len[2 * i] & 15) | (len[2 * i + 1] << 4));
+}
+void unpack_nibbles(const uint8_t *in128, uint8_t *len) {
+  for (int i = 0; i < 128; ++i) {
+    len[2 * i] = in128[i] & 15;
+    len[2 * i + 1] = in128[i] >> 4;
+  }
+}
+
 // Work-item geometry of one matrix (see nwc_format.h).
 struct Geo {
   int C = 0, R = 0, S = 0, W = 0, n_spans = 0;
@@ -232,9 +320,8 @@ inline uint32_t symbol_index(const void *w, int elem, int64_t idx) {
 }
 
 // Bits of one lane's stream: lead bits, its real codes, filler codes.
-uint64_t lane_bits(const void *w, int64_t n, int64_t k, int64_t ld, int elem, const CodeTable &tab,
+uint64_t lane_bits(const void *w, int64_t n, int64_t k, int64_t ld, int elem, const CodeTable &tab, uint64_t filler,
                    const Geo &g, const LaneSpan &ls) {
-  const uint64_t filler = elem == NWC_BF16 ? 2 : 5;
   uint64_t bits = NWC_LEAD_BITS;
   const int64_t real = ls.row < n ? std::max<int64_t>(0, std::min<int64_t>(k - ls.c0, g.C)) : 0;
   const int64_t base = ls.row * ld + ls.c0;
@@ -244,13 +331,13 @@ uint64_t lane_bits(const void *w, int64_t n, int64_t k, int64_t ld, int elem, co
 
 // Longest lane stream (in 32-bit words) of every item.
 std::vector<uint32_t> plan_rows(const void *w, int64_t n, int64_t k, int64_t ld, int elem, const CodeTable &tab,
-                                const Geo &g) {
+                                uint64_t filler, const Geo &g) {
   std::vector<uint32_t> rows(g.n_items, 1);
   parallel_for(g.n_items, [&](int64_t i0, int64_t i1) {
     for (int64_t it = i0; it < i1; ++it) {
       uint64_t maxbits = NWC_LEAD_BITS;
       for (int L = 0; L < NWC_LANES; ++L)
-        maxbits = std::max(maxbits, lane_bits(w, n, k, ld, elem, tab, g, lane_span(g, it, L)));
+        maxbits = std::max(maxbits, lane_bits(w, n, k, ld, elem, tab, filler, g, lane_span(g, it, L)));
       rows[it] = (uint32_t)nwc_ceil_div((int64_t)maxbits, 32);
     }
   });
@@ -313,17 +400,26 @@ int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_lane, int rows
 
 int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_lane, int rows_per_wave,
                void *blob, int64_t blob_cap, int64_t *blob_size) {
+  return nwc_encode_ex(w, n, k, ld, elem, NWC_CODER_UNARY, cols_per_lane, rows_per_wave, blob, blob_cap, blob_size);
+}
+
+int nwc_encode_ex(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int coder, int cols_per_lane,
+                  int rows_per_wave, void *blob, int64_t blob_cap, int64_t *blob_size) {
   if (!w || !blob || !blob_size) return NWC_ERR_ARG;
   if (elem != NWC_BF16 && elem != NWC_FP8_E4M3) return NWC_ERR_ARG;
+  if (coder != NWC_CODER_UNARY && coder != NWC_CODER_HUFFMAN) return NWC_ERR_ARG;
+  if (coder == NWC_CODER_HUFFMAN && elem != NWC_FP8_E4M3) return NWC_ERR_UNSUPPORTED;
+  const bool huff = coder == NWC_CODER_HUFFMAN;
   if (!valid_geometry_request(cols_per_lane, rows_per_wave)) return NWC_ERR_ARG;
   if (n <= 0 || k <= 0 || ld < k || n > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return NWC_ERR_SHAPE;
 
-  // 1. histogram of the ranked symbol over the real weights
-  const int alphabet = elem == NWC_BF16 ? 128 : 16;
-  std::vector<uint64_t> counts(alphabet, 0);
+  // 1. histogram of the symbol each code carries, over the real weights:
+  // the BF16 high byte, or the whole fp8 byte (the unary code ranks its 4-bit
+  // exponent field, the Huffman variant the byte itself)
+  std::vector<uint64_t> bytes(256, 0);
   {
     const int t = worker_count();
-    std::vector<std::vector<uint64_t>> part(t, std::vector<uint64_t>(alphabet, 0));
+    std::vector<std::vector<uint64_t>> part(t, std::vector<uint64_t>(256, 0));
     std::vector<std::thread> th;
     for (int i = 0; i < t; ++i)
       th.emplace_back([&, i] {
@@ -331,39 +427,54 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
         for (int64_t r = n * i / t; r < n * (i + 1) / t; ++r) {
           if (elem == NWC_BF16) {
             const uint16_t *row = (const uint16_t *)w + r * ld;
-            for (int64_t c = 0; c < k; ++c) h[(row[c] >> 8) & 0x7F]++;
+            for (int64_t c = 0; c < k; ++c) h[row[c] >> 8]++;
           } else {
             const uint8_t *row = (const uint8_t *)w + r * ld;
-            for (int64_t c = 0; c < k; ++c) h[(row[c] >> 3) & 15]++;
+            for (int64_t c = 0; c < k; ++c) h[row[c]]++;
           }
         }
       });
     for (auto &x : th) x.join();
     for (auto &h : part)
-      for (int s = 0; s < alphabet; ++s) counts[s] += h[s];
+      for (int s = 0; s < 256; ++s) bytes[s] += h[s];
   }
 
-  // 2. rank table and codewords
+  // 2. rank table (unary) or code lengths (Huffman), and codewords
   nwc_header_t hd;
   memset(&hd, 0, sizeof hd);
-  uint8_t sym_to_rank[128] = {0};
-  rank_table(counts.data(), alphabet, hd.rank_to_sym, sym_to_rank);
   CodeTable tab;
-  if (elem == NWC_BF16)
-    bf16_codes(sym_to_rank, tab);
-  else
-    fp8_codes(sym_to_rank, tab);
+  uint64_t filler_bits;
+  if (!huff) {
+    const int alphabet = elem == NWC_BF16 ? 128 : 16;
+    std::vector<uint64_t> counts(alphabet, 0);
+    for (int b = 0; b < 256; ++b) counts[elem == NWC_BF16 ? (b & 0x7F) : ((b >> 3) & 15)] += bytes[b];
+    uint8_t sym_to_rank[128] = {0};
+    rank_table(counts.data(), alphabet, hd.rank_to_sym, sym_to_rank);
+    if (elem == NWC_BF16)
+      bf16_codes(sym_to_rank, tab);
+    else
+      fp8_codes(sym_to_rank, tab);
+    filler_bits = elem == NWC_BF16 ? 2 : 5;  // rank 0, sign 0 (fp8: mantissa 0): all-zero bits
+  } else {
+    std::vector<uint64_t> cons(bytes);
+    if (!cons[0]) cons[0] = 1;  // the filler byte always gets a codeword
+    uint8_t len[256];
+    huffman_lengths(cons.data(), 256, NWC_HUFF_MAX_LEN, len);
+    pack_nibbles(len, hd.rank_to_sym);
+    huffman_codes(len, tab);
+    filler_bits = tab.len[0];
+  }
 
   // 3. work-item geometry; fewer waves per workgroup (more column spans) if
   // the staged code rows of a workgroup would not fit the decoder's LDS.
   RowEstimate est;
   {
     double total = 0, s1 = 0, s2 = 0;
-    for (int sy = 0; sy < alphabet; ++sy) {
-      const double l = tab.len[elem == NWC_BF16 ? sy : (sy << 3)];
-      total += (double)counts[sy];
-      s1 += (double)counts[sy] * l;
-      s2 += (double)counts[sy] * l * l;
+    for (int b = 0; b < 256; ++b) {
+      const double l = tab.len[b];
+      total += (double)bytes[b];
+      s1 += (double)bytes[b] * l;
+      s2 += (double)bytes[b] * l * l;
     }
     est.mean = s1 / total;
     est.var = std::max(0.0, s2 / total - est.mean * est.mean);
@@ -371,7 +482,7 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   Geo g = auto_geo(n, k, cols_per_lane, rows_per_wave, est);
   std::vector<uint32_t> rows;
   for (int mw = NWC_MAX_WAVES;; --mw) {
-    rows = plan_rows(w, n, k, ld, elem, tab, g);
+    rows = plan_rows(w, n, k, ld, elem, tab, filler_bits, g);
     const uint32_t mx = *std::max_element(rows.begin(), rows.end());
     if (mx > NWC_ROWS_CAP) return NWC_ERR_UNSUPPORTED;  // cannot happen: C <= 64 needs <= 33 rows
     if (lds_need(g, mx) <= NWC_LDS_BUDGET) break;
@@ -393,7 +504,7 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   hd.n_rowgroups = (uint32_t)g.n_rg;
   hd.n_items = (uint32_t)g.n_items;
   hd.max_rows = *std::max_element(rows.begin(), rows.end());
-  hd.escape_r = NWC_ESCAPE_R;
+  hd.escape_r = huff ? 0u : NWC_ESCAPE_R;
   hd.off_lut = NWC_HEADER_BYTES;
   hd.off_items = hd.off_lut + NWC_LUT_BYTES;
   hd.off_mant = hd.off_items + (uint64_t)nwc_round_up(g.n_items * 8, 256);
@@ -411,9 +522,8 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   if ((int64_t)hd.total_bytes > blob_cap) return NWC_ERR_CAPACITY;
 
   // 5. coded size of the real weights (sum of codeword lengths + raw bytes)
-  // (codeword length depends on the rank only, not on sign or fp8 mantissa)
   uint64_t coded = 0;
-  for (int s = 0; s < alphabet; ++s) coded += counts[s] * tab.len[elem == NWC_BF16 ? s : (s << 3)];
+  for (int b = 0; b < 256; ++b) coded += bytes[b] * tab.len[b];
   if (elem == NWC_BF16) coded += 8ull * (uint64_t)n * (uint64_t)k;
   hd.coded_bits = coded;
 
@@ -422,17 +532,23 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
   memset(out, 0, hd.off_code);
   memcpy(out, &hd, sizeof hd);
   uint32_t *lut = (uint32_t *)(out + hd.off_lut);
-  if (elem == NWC_BF16)
+  if (elem == NWC_BF16) {
     build_lut_bf16(hd.rank_to_sym, lut);
-  else
+  } else if (huff) {
+    uint8_t len[256];
+    unpack_nibbles(hd.rank_to_sym, len);
+    build_lut_fp8_huffman(len, lut);
+  } else {
     build_lut_fp8(hd.rank_to_sym, lut);
+  }
   uint32_t *items = (uint32_t *)(out + hd.off_items);
   for (int64_t i = 0; i < g.n_items; ++i) {
     items[2 * i] = code_off[i];
     items[2 * i + 1] = rows[i];
   }
 
-  // 7. code and mantissa planes, one item per task (fillers stay zero)
+  // 7. code and mantissa planes, one item per task (unary fillers are zero
+  // bits, so they stay as cleared; Huffman fillers are byte 0x00's codeword)
   parallel_for(g.n_items, [&](int64_t i0, int64_t i1) {
     for (int64_t it = i0; it < i1; ++it) {
       uint32_t *code = (uint32_t *)(out + hd.off_code + code_off[it]);
@@ -444,13 +560,13 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
       }
       for (int L = 0; L < NWC_LANES; ++L) {
         const LaneSpan ls = lane_span(g, it, L);
-        if (ls.row >= n || ls.c0 >= k) continue;
-        const int64_t nc = std::min<int64_t>(k - ls.c0, g.C);
+        const int64_t nc = (ls.row >= n || ls.c0 >= k) ? 0 : std::min<int64_t>(k - ls.c0, g.C);
+        if (nc == 0 && !huff) continue;
         uint64_t acc = 0;
         uint32_t nbits = NWC_LEAD_BITS, word = 0;
-        for (int64_t c = 0; c < nc; ++c) {
+        for (int64_t c = 0; c < (huff ? (int64_t)g.C : nc); ++c) {
           const int64_t idx = ls.row * ld + ls.c0 + c;
-          const uint32_t sym = symbol_index(w, elem, idx);
+          const uint32_t sym = c < nc ? symbol_index(w, elem, idx) : 0u;  // Huffman filler: byte 0x00
           acc |= (uint64_t)tab.val[sym] << nbits;
           nbits += tab.len[sym];
           if (nbits >= 32) {
@@ -459,7 +575,7 @@ int nwc_encode(const void *w, int64_t n, int64_t k, int64_t ld, int elem, int co
             nbits -= 32;
             ++word;
           }
-          if (mant) mant[((c >> 4) * NWC_LANES + L) * 16 + (c & 15)] = (uint8_t)((const uint16_t *)w)[idx];
+          if (mant && c < nc) mant[((c >> 4) * NWC_LANES + L) * 16 + (c & 15)] = (uint8_t)((const uint16_t *)w)[idx];
         }
         if (nbits) code[(uint64_t)word * NWC_LANES + L] = (uint32_t)acc;
       }
@@ -491,6 +607,7 @@ int nwc_blob_info(const void *blob, int64_t blob_bytes, nwc_info *info) {
   info->code_bytes = h.code_bytes;
   info->mant_bytes = h.mant_bytes;
   info->table_bytes = h.off_mant;
+  info->coder = h.escape_r == 0 ? NWC_CODER_HUFFMAN : NWC_CODER_UNARY;
   memcpy(info->rank_to_sym, h.rank_to_sym, 128);
   return NWC_OK;
 }
@@ -504,21 +621,35 @@ int nwc_blob_check(const void *blob, int64_t blob_bytes) {
   if (st != NWC_OK) return st;
   if ((uint64_t)blob_bytes < h.total_bytes) return NWC_ERR_CAPACITY;
   const uint8_t *b = (const uint8_t *)blob;
-  // The rank table orders every symbol once (128 exponent/sign symbols, or
-  // the 16 fp8 exponent fields).
-  const int n_sym = h.elem == NWC_BF16 ? 128 : 16;
-  bool seen[128] = {};
-  for (int r = 0; r < n_sym; ++r) {
-    const int sym = h.rank_to_sym[r];
-    if (sym >= n_sym || seen[sym]) return NWC_ERR_FORMAT;
-    seen[sym] = true;
-  }
-  // The decode table is the one that rank table defines.
   std::vector<uint32_t> lut(NWC_LUT_ENTRIES);
-  if (h.elem == NWC_BF16)
-    build_lut_bf16(h.rank_to_sym, lut.data());
-  else
-    build_lut_fp8(h.rank_to_sym, lut.data());
+  if (h.escape_r == 0) {
+    // Huffman variant: lengths at most 12 bits, Kraft sum at most one (a
+    // prefix code), a codeword for the filler byte 0x00.
+    uint8_t len[256];
+    unpack_nibbles(h.rank_to_sym, len);
+    uint64_t kraft = 0;  // in units of 2^-12
+    for (int b = 0; b < 256; ++b) {
+      if (len[b] > NWC_HUFF_MAX_LEN) return NWC_ERR_FORMAT;
+      if (len[b]) kraft += 1ull << (NWC_HUFF_MAX_LEN - len[b]);
+    }
+    if (!len[0] || kraft > (1ull << NWC_HUFF_MAX_LEN)) return NWC_ERR_FORMAT;
+    build_lut_fp8_huffman(len, lut.data());
+  } else {
+    // The rank table orders every symbol once (128 exponent/sign symbols, or
+    // the 16 fp8 exponent fields).
+    const int n_sym = h.elem == NWC_BF16 ? 128 : 16;
+    bool seen[128] = {};
+    for (int r = 0; r < n_sym; ++r) {
+      const int sym = h.rank_to_sym[r];
+      if (sym >= n_sym || seen[sym]) return NWC_ERR_FORMAT;
+      seen[sym] = true;
+    }
+    if (h.elem == NWC_BF16)
+      build_lut_bf16(h.rank_to_sym, lut.data());
+    else
+      build_lut_fp8(h.rank_to_sym, lut.data());
+  }
+  // The decode table is the one the rank table (or the code lengths) defines.
   if (memcmp(lut.data(), b + h.off_lut, NWC_LUT_BYTES) != 0) return NWC_ERR_FORMAT;
   // Every item's code rows lie inside the code plane, whole 256-byte rows,
   // at least one and at most max_rows (the kernels size their buffers by it).

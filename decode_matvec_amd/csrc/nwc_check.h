@@ -36,7 +36,8 @@ static inline int nwc_check_header(const nwc_header_t *h) {
   if (sp * W < waves_per_row || sp * (W - 1) >= waves_per_row) return NWC_ERR_FORMAT;
   if (h->n_rowgroups != nwc_ceil_div(h->n, R)) return NWC_ERR_FORMAT;
   if ((int64_t)h->n_items != (int64_t)h->n_rowgroups * sp * W) return NWC_ERR_FORMAT;
-  if (h->max_rows < 1 || h->max_rows > NWC_ROWS_CAP || h->escape_r != NWC_ESCAPE_R) return NWC_ERR_FORMAT;
+  if (h->max_rows < 1 || h->max_rows > NWC_ROWS_CAP) return NWC_ERR_FORMAT;
+  if (h->escape_r != NWC_ESCAPE_R && !(h->escape_r == 0 && h->elem == NWC_FP8_E4M3)) return NWC_ERR_FORMAT;
   if (nwc_lds_bytes(h) > NWC_LDS_BUDGET) return NWC_ERR_FORMAT;
   const uint64_t items_bytes = (uint64_t)nwc_round_up((int64_t)h->n_items * 8, 256);
   const uint64_t mant = h->elem == NWC_BF16 ? (uint64_t)h->n_items * NWC_LANES * C : 0;

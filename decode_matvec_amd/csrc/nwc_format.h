@@ -28,7 +28,8 @@
 //   lane L: row = row_group*R + L/S, slice q = (span*W + wave)*S + L%S
 //
 // Fillers.  Columns at or past K and rows at or past N are fillers: zero code
-// bits, which decode as rank 0 with sign 0, and zero mantissa bytes.  A filler
+// bits, which decode as rank 0 with sign 0, and zero mantissa bytes (the
+// Huffman variant writes byte 0x00's codeword instead).  A filler
 // therefore decodes to a finite value (BF16 exponent field 2*symbol <= 254;
 // fp8 mantissa 0 is never NaN) and adds exactly zero against the zero
 // activation the kernel uses past column K.
@@ -51,16 +52,28 @@
 // Decode table (fp8): one code per peek:
 //   bits 0..15 the value as BF16, 16..23 the fp8 byte, 24..30 bits used,
 //   31 = 1 if the code is an escape (longer than 12 bits).
+//
+// Coder variant (escape_r == 0, fp8 only): a length-limited canonical Huffman
+// code over whole fp8 bytes.  Codeword lengths (at most NWC_HUFF_MAX_LEN = 12
+// bits, optimal for the matrix's byte histogram, found by package-merge) are
+// stored as nibbles in rank_to_sym; codewords are canonical (bytes in order of
+// (length, value); the first is all zeros; each next is the previous plus one,
+// shifted left by the growth in length) and written most significant bit
+// first.  Byte 0x00 always has a codeword: it is the filler of this variant
+// (fillers are written as its codeword, so they decode to +0).  Every
+// codeword fits the 12-bit peek, so the fp8 decode table above decodes every
+// code and has no escapes.
 #pragma once
 #include <stdint.h>
 
 #define NWC_MAGIC 0x3143574Eu /* "NWC1" */
-#define NWC_FORMAT_VERSION 3u
+#define NWC_FORMAT_VERSION 4u
 #define NWC_HEADER_BYTES 256
 #define NWC_LANES 64
 #define NWC_LUT_ENTRIES 4096
 #define NWC_LUT_BYTES (NWC_LUT_ENTRIES * 4)
 #define NWC_ESCAPE_R 8
+#define NWC_HUFF_MAX_LEN 12 /* longest Huffman codeword: the decode table's peek */
 #define NWC_LEAD_BITS 2
 #define NWC_MAX_COLS 64     /* cols_per_lane: multiple of 16 in [16, 64] */
 #define NWC_MAX_WAVES 16    /* waves per workgroup (1024 threads) */
@@ -86,12 +99,14 @@ typedef struct nwc_header_t {
   uint32_t n_rowgroups;      /* ceil(n / R) */
   uint32_t n_items;          /* n_rowgroups * n_spans * W */
   uint32_t max_rows;         /* largest code_rows of any item */
-  uint32_t escape_r;         /* 8 */
+  uint32_t escape_r;         /* 8: unary rank code; 0: Huffman over fp8 bytes */
   uint64_t coded_bits;       /* code bits of the real weights (+ 8 per BF16 weight) */
   uint64_t off_lut, off_items, off_mant, off_code;
   uint64_t total_bytes;
   uint64_t code_bytes, mant_bytes;
-  uint8_t rank_to_sym[128];  /* 128 BF16 symbols, or 16 fp8 exponent fields */
+  uint8_t rank_to_sym[128];  /* 128 BF16 symbols, or 16 fp8 exponent fields;
+                                Huffman: codeword length of byte b in nibble b
+                                (byte b/2, low nibble for even b), 0 = none */
 } nwc_header_t;
 
 #ifdef __cplusplus

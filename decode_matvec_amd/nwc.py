@@ -18,13 +18,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnwc.so")
 
 NWC_BF16 = 0
 NWC_FP8_E4M3 = 1
+NWC_CODER_UNARY = 0
+NWC_CODER_HUFFMAN = 1
 HEADER_BYTES = 256
 GROUP_MAX = 12
 
 STATUS = {0: "NWC_OK", -1: "NWC_ERR_ARG", -2: "NWC_ERR_SHAPE", -3: "NWC_ERR_CAPACITY",
           -4: "NWC_ERR_FORMAT", -5: "NWC_ERR_HIP", -6: "NWC_ERR_UNSUPPORTED"}
 
-EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_blob_info", "nwc_blob_check",
+EXPORTS = ("nwc_version", "nwc_status_string", "nwc_encode_bound", "nwc_encode", "nwc_encode_ex", "nwc_blob_info", "nwc_blob_check",
            "nwc_workspace_size", "nwc_matvec", "nwc_matvec_noalloc", "nwc_matvec_group", "nwc_matvec_batch", "nwc_dequant", "nwc_gather", "nwc_stream_read",
            "nwc_bf16_gemv", "nwc_bf16_gemv_group")
 
@@ -39,7 +41,7 @@ class NWCInfo(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("elem", ctypes.c_int32),
                 ("cols_per_lane", ctypes.c_int32), ("rows_per_wave", ctypes.c_int32),
                 ("waves_per_group", ctypes.c_int32), ("n_spans", ctypes.c_int32), ("n_items", ctypes.c_int32),
-                ("max_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("coder", ctypes.c_int32),
                 ("coded_bits", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
                 ("code_bytes", ctypes.c_uint64), ("mant_bytes", ctypes.c_uint64),
                 ("table_bytes", ctypes.c_uint64), ("rank_to_sym", ctypes.c_uint8 * 128)]
@@ -73,6 +75,7 @@ def _load():
         "nwc_status_string": ([ci], ctypes.c_char_p),
         "nwc_encode_bound": ([i64, i64, ci, ci, ci, ctypes.POINTER(i64)], ci),
         "nwc_encode": ([vp, i64, i64, i64, ci, ci, ci, vp, i64, ctypes.POINTER(i64)], ci),
+        "nwc_encode_ex": ([vp, i64, i64, i64, ci, ci, ci, ci, vp, i64, ctypes.POINTER(i64)], ci),
         "nwc_blob_info": ([vp, i64, ctypes.POINTER(NWCInfo)], ci),
         "nwc_blob_check": ([vp, i64], ci),
         "nwc_workspace_size": ([vp, ctypes.POINTER(i64)], ci),
@@ -119,10 +122,12 @@ def encode_bound(n: int, k: int, elem: int = NWC_BF16, cols_per_lane: int = 0, r
     return out.value
 
 
-def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_lane: int = 0, rows_per_wave: int = 0) -> np.ndarray:
+def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_lane: int = 0, rows_per_wave: int = 0,
+           coder: int = NWC_CODER_UNARY) -> np.ndarray:
     """Encode a host matrix (uint16 BF16 patterns or uint8 fp8 bytes) -> uint8 blob.
 
-    cols_per_lane / rows_per_wave: 0 lets the library choose the work-item geometry."""
+    cols_per_lane / rows_per_wave: 0 lets the library choose the work-item geometry.
+    coder: NWC_CODER_UNARY (the pages' code) or NWC_CODER_HUFFMAN (fp8 bytes, length-limited Huffman)."""
     want = np.uint16 if elem == NWC_BF16 else np.uint8
     if w.dtype != want or w.ndim != 2:
         raise TypeError(f"expected a 2-D {np.dtype(want).name} array, got {w.dtype} {w.shape}")
@@ -133,8 +138,8 @@ def encode(w: np.ndarray, elem: int = NWC_BF16, cols_per_lane: int = 0, rows_per
     cap = encode_bound(n, k, elem, cols_per_lane, rows_per_wave)
     blob = np.empty(cap, dtype=np.uint8)
     size = ctypes.c_int64()
-    _check("nwc_encode", lib.nwc_encode(_host_ptr(w), n, k, ld, elem, cols_per_lane, rows_per_wave, _host_ptr(blob),
-                                        cap, ctypes.byref(size)))
+    _check("nwc_encode_ex", lib.nwc_encode_ex(_host_ptr(w), n, k, ld, elem, coder, cols_per_lane, rows_per_wave,
+                                              _host_ptr(blob), cap, ctypes.byref(size)))
     return blob[:size.value].copy()
 
 

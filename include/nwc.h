@@ -52,6 +52,13 @@ typedef enum nwc_elem {
   NWC_FP8_E4M3 = 1  /* input: uint8 e4m3fn bytes (already quantized) */
 } nwc_elem;
 
+typedef enum nwc_coder {
+  NWC_CODER_UNARY = 0,   /* the pages' code: frequency-ranked unary rank + raw
+                            sign (+ raw fp8 mantissa bits), escape after 8 ranks */
+  NWC_CODER_HUFFMAN = 1  /* fp8 only: length-limited (12-bit) canonical Huffman
+                            code over whole fp8 bytes */
+} nwc_coder;
+
 /* Blob metadata, filled by nwc_blob_info. */
 typedef struct nwc_info {
   int64_t n, k;
@@ -62,14 +69,16 @@ typedef struct nwc_info {
   int32_t n_spans;         /* workgroups along one row (1 unless k > 16*64*C/R) */
   int32_t n_items;         /* work items (one wave each) */
   int32_t max_rows;        /* longest item code column, in 32-bit words */
-  int32_t reserved;
+  int32_t coder;           /* nwc_coder of the blob */
   uint64_t coded_bits;     /* sum of codeword lengths of the real weights, plus
                               8 raw mantissa bits per BF16 weight */
   uint64_t total_bytes;    /* whole blob */
   uint64_t code_bytes;     /* code plane incl. per-item zero padding */
   uint64_t mant_bytes;     /* mantissa plane (0 for fp8) */
   uint64_t table_bytes;    /* header + decode table + item table */
-  uint8_t rank_to_sym[128];/* frequency rank -> symbol (16 used for fp8) */
+  uint8_t rank_to_sym[128];/* frequency rank -> symbol (16 used for fp8); for
+                              NWC_CODER_HUFFMAN the codeword length of byte b
+                              in nibble b (low nibble of byte b/2 for even b) */
 } nwc_info;
 
 /* Library version (NWC_VERSION of the build). */
@@ -96,6 +105,18 @@ int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_lane, int rows
  * byte is encoded losslessly.  Uses up to hardware_concurrency host threads. */
 int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_lane,
                int rows_per_wave, void *blob, int64_t blob_cap, int64_t *blob_size);
+
+/* nwc_encode with a choice of coder.  NWC_CODER_UNARY is nwc_encode.
+ * NWC_CODER_HUFFMAN (fp8 only; NWC_ERR_UNSUPPORTED for BF16) is the coder
+ * variant the fp8 model card's "coded whole" bytes leave room for: every fp8
+ * byte of the matrix gets an optimal prefix codeword of at most 12 bits
+ * (package-merge over the byte histogram), canonical order, most significant
+ * bit first; byte 0x00 always has a codeword and pads the layout.  Every
+ * codeword fits the decoders' 12-bit table lookup, so no code needs an
+ * escape.  The device entry points decode both coders.  coder: nwc_coder;
+ * other arguments and errors as nwc_encode. */
+int nwc_encode_ex(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, int coder, int cols_per_lane,
+                  int rows_per_wave, void *blob, int64_t blob_cap, int64_t *blob_size);
 
 /* Validate a blob header (host pointer, at least NWC_HEADER_BYTES) and
  * describe it.  blob_bytes: bytes available at `blob` (>= header bytes). */

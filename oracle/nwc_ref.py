@@ -423,12 +423,19 @@ def codeword_huffman(code: int, length: int) -> list:
     return [(code >> (length - 1 - i)) & 1 for i in range(length)]
 
 
-def encode_fp8_huffman(q_u8, max_len: int = HUFF_MAX_LEN) -> dict:
-    """Per-row streams of the fp8 bytes under the matrix's length-limited canonical Huffman code."""
+def encode_fp8_huffman(q_u8, max_len: int = HUFF_MAX_LEN, filler_codeword: bool = True) -> dict:
+    """Per-row streams of the fp8 bytes under the matrix's length-limited canonical Huffman code.
+
+    filler_codeword: give byte 0x00 a codeword even when it does not occur
+    (counted once) -- the library pads its lane streams with that byte; the
+    oracle's own streams need no padding, so a worked example may turn it off."""
     q = np.ascontiguousarray(q_u8, dtype=np.uint8)
     n, k = q.shape
     counts = np.bincount(q.reshape(-1).astype(np.int64), minlength=256)
-    lengths = huffman_lengths_limited(counts, max_len)
+    cons = counts.copy()
+    if filler_codeword and cons[0] == 0:
+        cons[0] = 1
+    lengths = huffman_lengths_limited(cons, max_len)
     codes = canonical_codes(lengths)
     val = np.zeros(256, dtype=np.uint32)
     ln = np.zeros(256, dtype=np.int64)

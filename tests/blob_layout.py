@@ -58,15 +58,37 @@ def _parse_fp8(bits, pos, r2s):
     return (s << 7) | (E << 3) | M, pos + 16
 
 
+def huffman_lengths(h) -> list:
+    """Codeword length of each fp8 byte of a Huffman-variant blob (nibbles of the rank_to_sym field)."""
+    r = h["rank_to_sym"]
+    return [int(r[b // 2]) >> (4 * (b & 1)) & 15 for b in range(256)]
+
+
+def _huffman_parser(h):
+    codes = O.canonical_codes(huffman_lengths(h))
+    by_bits = {tuple(O.codeword_huffman(c, l)): s for s, (c, l) in codes.items()}
+
+    def parse(bits, pos):
+        for l in range(1, O.HUFF_MAX_LEN + 1):
+            s = by_bits.get(tuple(bits[pos:pos + l]))
+            if s is not None:
+                return s, pos + l
+        raise AssertionError("no codeword")
+    return parse
+
+
 def decode_blob(blob: np.ndarray) -> np.ndarray:
     """Whole matrix from a library blob (uint16 BF16 patterns or uint8 fp8 bytes).
 
     Also asserts the filler convention: every lane stream starts with two zero
-    bits, and stream bits past a lane's real columns, and mantissa bytes of
-    filler columns, are zero."""
+    bits, and stream bits past a lane's real columns (after the Huffman
+    variant's filler codewords of byte 0x00), and mantissa bytes of filler
+    columns, are zero."""
     h = header(blob)
     n, k, C = h["n"], h["k"], h["cols_per_lane"]
     fp8 = h["elem"] == 1
+    huff = fp8 and h["escape_r"] == 0
+    parse_h = _huffman_parser(h) if huff else None
     r2s = np.array(h["rank_to_sym"][: 16 if fp8 else 128], dtype=np.int64)
     out = np.zeros((n, k), dtype=np.uint8 if fp8 else np.uint16)
     seen = np.zeros((n, k), dtype=bool)
@@ -79,13 +101,20 @@ def decode_blob(blob: np.ndarray) -> np.ndarray:
             pos = 2
             padded = list(bits) + [0] * 32
             for c in range(real):
-                if fp8:
+                if huff:
+                    b, pos = parse_h(padded, pos)
+                    out[row, c0 + c] = b
+                elif fp8:
                     b, pos = _parse_fp8(padded, pos, r2s)
                     out[row, c0 + c] = b
                 else:
                     s, e, pos = O.parse_one_bf16(padded, pos, r2s)
                     out[row, c0 + c] = (s << 15) | (e << 8) | int(mant_byte(blob, h, item, L, c))
                 seen[row, c0 + c] = True
+            if huff:   # fillers: byte 0x00's codeword up to C codes per lane
+                for c in range(real, C):
+                    b, pos = parse_h(padded, pos)
+                    assert b == 0, (item, L, c)
             assert not np.any(bits[pos:]), (item, L)
             if not fp8:
                 for c in range(real, C):

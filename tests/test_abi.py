@@ -425,3 +425,93 @@ def test_matvec_noalloc_rejects_bad_arguments_before_any_gpu_call():
     assert L.nwc_matvec_noalloc(big.ctypes.data, fake, fake, None, fake, None) == -3
     fits = _grown_header(hdr, 200000)
     assert nwc.workspace_size(fits) <= nwc.NOALLOC_SCRATCH_BYTES
+
+
+# ----------------------------------------------------------------- Huffman coder variant (fp8 bytes)
+def _fp8_mats():
+    q1, _ = S.fp8_quantize(S.normal_bf16(C.SINGLE["w_seed"], (C.SINGLE["n"], C.SINGLE["k"]), C.SINGLE["sigma"]))
+    qt, _ = S.fp8_quantize(S.odd_shape_matrix(1, "t3")[0])
+    qz = np.full((5, 40), 0x38, np.uint8)   # one byte value: 0x00 added as the filler codeword
+    return [("single_1024", q1), ("t3_1000x3001", qt), ("all_bytes", S.all_bytes_fp8(3)), ("one_value", qz)]
+
+
+@pytest.mark.parametrize("name,q", _fp8_mats(), ids=lambda v: v if isinstance(v, str) else "")
+def test_huffman_encoder_size_equals_the_oracle_optimum(name, q):
+    blob = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=nwc.NWC_CODER_HUFFMAN)
+    info = nwc.blob_info(blob)
+    assert info["coder"] == nwc.NWC_CODER_HUFFMAN
+    lengths = BL.huffman_lengths(BL.header(blob))
+    assert max(lengths) <= 12 and lengths[0] > 0 and O.kraft_sum(lengths) <= 1
+    counts = np.bincount(q.reshape(-1), minlength=256)
+    assert all(lengths[b] > 0 for b in range(256) if counts[b])
+    # Optimal length-limited codes have one total size: the library's package-merge and the oracle's agree.
+    enc = O.encode_fp8_huffman(q)
+    assert info["coded_bits"] == enc["coded_bits"] == int((counts * np.array(lengths)).sum())
+    nwc.blob_check(blob)
+
+
+@pytest.mark.parametrize("shape,cols,rows,seed", [((70, 333), 16, 8, 1), ((130, 100), 0, 0, 2), ((3, 600), 64, 1, 3),
+                                                  ((9, 1000), 48, 2, 5), ((2, 66000), 64, 1, 7)])
+def test_huffman_blob_layout_decodes_to_input(shape, cols, rows, seed):
+    q, _ = S.fp8_quantize(S.inject_rare(S.student_t_bf16(seed, shape), seed + 7, frac=0.02))
+    blob = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_lane=cols, rows_per_wave=rows, coder=nwc.NWC_CODER_HUFFMAN)
+    assert np.array_equal(BL.decode_blob(blob), q)
+
+
+def test_decode_table_huffman_against_oracle():
+    q, _ = S.fp8_quantize(S.normal_bf16(1, (256, 256), 0.02))
+    blob = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=nwc.NWC_CODER_HUFFMAN)
+    lut = BL.lut(blob)
+    codes = O.canonical_codes(BL.huffman_lengths(BL.header(blob)))
+    import torch
+    hits = 0
+    for b, (c, l) in codes.items():
+        bits = O.codeword_huffman(c, l)
+        first = sum(v << i for i, v in enumerate(bits))   # stream order, first bit at bit 0
+        bf = torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.bfloat16)
+        want_bf = int(bf.view(torch.int16).item()) & 0xFFFF
+        for p in range(first, 4096, 1 << l):
+            e = int(lut[p])
+            if torch.isnan(bf).item():
+                assert (e & 0x7F80) == 0x7F80 and (e & 0x7F) != 0
+            else:
+                assert e & 0xFFFF == want_bf
+            assert (e >> 16) & 0xFF == b and (e >> 24) == l
+            hits += 1
+    assert hits == 4096   # a complete code: every 12-bit peek starts exactly one codeword
+
+
+def test_huffman_blob_check_rejects_bad_lengths():
+    q, _ = S.fp8_quantize(S.normal_bf16(2, (64, 300), 0.02))
+    blob = nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=nwc.NWC_CODER_HUFFMAN)
+    nwc.blob_check(blob)
+    h = BL.header(blob)
+    lengths = BL.huffman_lengths(h)
+    used = [b for b in range(256) if lengths[b]]
+
+    def with_lengths(ls):
+        bad = blob.copy()
+        for i in range(128):
+            bad[128 + i] = (ls[2 * i] & 15) | (ls[2 * i + 1] << 4)
+        return bad
+
+    ls = list(lengths)
+    ls[used[-1]] = 13                      # longer than the 12-bit peek
+    with pytest.raises(nwc.NWCError):
+        nwc.blob_check(with_lengths(ls))
+    ls = list(lengths)
+    ls[0] = 0                              # no filler codeword
+    with pytest.raises(nwc.NWCError):
+        nwc.blob_check(with_lengths(ls))
+    ls = list(lengths)
+    ls[[b for b in range(256) if not lengths[b]][0]] = 1    # Kraft sum above one
+    with pytest.raises(nwc.NWCError):
+        nwc.blob_check(with_lengths(ls))
+    ls = list(lengths)
+    a, b = used[1], used[2]
+    ls[a], ls[b] = ls[b], ls[a]            # a valid code, but not the one the decode table holds
+    if ls != lengths:
+        with pytest.raises(nwc.NWCError):
+            nwc.blob_check(with_lengths(ls))
+    with pytest.raises(nwc.NWCError):      # Huffman only for fp8
+        nwc.encode(S.normal_bf16(2, (4, 8), 0.02), coder=nwc.NWC_CODER_HUFFMAN)

@@ -240,28 +240,66 @@ def test_exact_special_cases():
 
 
 # ----------------------------------------------------------------- fp8 variant of the single matrix
-def test_fp8_single_matrix():
+# Both coders of the fp8 bytes: the pages' unary rank code and the
+# length-limited Huffman variant (the same kernels decode both).
+FP8_CODERS = [nwc.NWC_CODER_UNARY, nwc.NWC_CODER_HUFFMAN]
+
+
+@pytest.mark.parametrize("coder", FP8_CODERS)
+def test_fp8_single_matrix(coder):
     w = S.normal_bf16(C.SINGLE["w_seed"], (1024, 1024), C.SINGLE["sigma"])
     x = S.activation_bf16(C.SINGLE["x_seed"], 1024)
     q, sc = S.fp8_quantize(w)
+    want = O.decode_fp8(O.encode_fp8(q)) if coder == nwc.NWC_CODER_UNARY else O.decode_fp8_huffman(
+        O.encode_fp8_huffman(q))
+    assert np.array_equal(want, q)
     for cols, rows in ((0, 0), (16, 64), (32, 8), (64, 1)):
-        dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_lane=cols, rows_per_wave=rows), DEV)
-        assert np.array_equal(dequant_host(dm), O.decode_fp8(O.encode_fp8(q)))
+        print(f"case fp8 coder={coder} cols={cols} rows={rows}", flush=True)
+        dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, cols_per_lane=cols, rows_per_wave=rows,
+                                         coder=coder), DEV)
+        assert np.array_equal(dequant_host(dm), want)
         y_ref, A = O.matvec_fp8_ref(q, sc, x)
         check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8")
+        ids = np.array([0, 1023, 7, 7, 512], dtype=np.int64)
+        out = torch.full((len(ids), 1024), 0xAB, dtype=torch.uint8, device=DEV)
+        dm.gather(torch.from_numpy(ids).to(DEV), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), q[ids])
 
 
-def test_fp8_all_bytes_and_odd():
+@pytest.mark.parametrize("coder", FP8_CODERS)
+def test_fp8_all_bytes_and_odd(coder):
     q = S.all_bytes_fp8(5)
-    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV)
+    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=coder), DEV)
     assert np.array_equal(dequant_host(dm), q)
     w = S.inject_rare(S.student_t_bf16(71, (1000, 3001)), 72)
     q, sc = S.fp8_quantize(w)
     x = S.activation_bf16(73, 3001)
-    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3), DEV)
+    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=coder), DEV)
     assert np.array_equal(dequant_host(dm), q)
     y_ref, A = O.matvec_fp8_ref(q, sc, x)
     check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8 odd")
+
+
+def test_fp8_huffman_full_size_and_one_value():
+    # A Qwen3-4B gate-shaped fp8 matrix (9728 x 2560) under the Huffman
+    # variant: every byte dequantized bit for bit, every output in tolerance;
+    # and a matrix of one byte value, whose code is that byte plus the filler.
+    w = S.blocked_normal_bf16(C.qwen3_seed(0, 4)[0], (9728, 2560), np.float32(C.sigma_for(2560)))
+    q, sc = S.fp8_quantize(w)
+    x = S.activation_bf16(C.qwen3_seed(0, 4)[1], 2560)
+    dm = nwc.DeviceMatrix(nwc.encode(q, elem=nwc.NWC_FP8_E4M3, coder=nwc.NWC_CODER_HUFFMAN), DEV)
+    assert np.array_equal(dequant_host(dm), q)
+    from oracle import fast as F
+    y_ref, A = F.matvec_fp8(q, sc, x)
+    check_tol(run_matvec(dm, x, sc), y_ref, A, "fp8 huffman 9728x2560")
+    q1 = np.full((33, 70), 0xB8, np.uint8)
+    sc1 = np.ones(33, np.float32)
+    x1 = S.activation_bf16(74, 70)
+    d1 = nwc.DeviceMatrix(nwc.encode(q1, elem=nwc.NWC_FP8_E4M3, coder=nwc.NWC_CODER_HUFFMAN), DEV)
+    assert np.array_equal(dequant_host(d1), q1)
+    y_ref, A = O.matvec_fp8_ref(q1, sc1, x1)
+    check_tol(run_matvec(d1, x1, sc1), y_ref, A, "fp8 huffman one value")
 
 
 # ----------------------------------------------------------------- small batches

@@ -185,8 +185,10 @@ def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16, with_fused=False
     return stack, head, h0.view(torch.bfloat16)
 
 
-def qwen25_step(torch, stack, head, h0, linear, fused=False):
-    """One batch-1 decode step.  linear(m, x_bf16) -> fp32 output of matrix m.
+def qwen25_step(torch, stack, head, h0, linear, fused=False, group=None):
+    """One batch-1 decode step.  linear(m, x_bf16) -> fp32 output of matrix m;
+    group(ms, x_bf16) -> fp32 outputs of the matrices ms, which read the same
+    input (q, k, v; gate, up), in one launch.
     As in the Qwen2 architecture, RMS norms (unit weight) precede attention,
     the MLP and the lm_head; the residual stream stays fp32.  Attention at
     context length 1 returns v for every query head (softmax over one
@@ -201,6 +203,8 @@ def qwen25_step(torch, stack, head, h0, linear, fused=False):
         hb = norm(h)
         if fused:  # q||k||v and gate||up as one matvec each (outputs split by rows)
             v = linear(L["qkv"], hb)[L["q"]["n"] + L["k"]["n"]:]
+        elif group is not None:
+            v = group([L["q"], L["k"], L["v"]], hb)[2]
         else:
             linear(L["q"], hb)
             linear(L["k"], hb)
@@ -211,6 +215,8 @@ def qwen25_step(torch, stack, head, h0, linear, fused=False):
         if fused:
             gu = linear(L["gate_up"], hb)
             gate, up = gu[:L["gate"]["n"]], gu[L["gate"]["n"]:]
+        elif group is not None:
+            gate, up = group([L["gate"], L["up"]], hb)
         else:
             gate, up = linear(L["gate"], hb), linear(L["up"], hb)
         act = (F.silu(gate) * up).to(torch.bfloat16)
@@ -240,8 +246,16 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
         torch.cuda.synchronize()
         return g
 
-    g_step = graph_of(lambda: qwen25_step(torch, stack, head, h0, nwc_linear))
+    def nwc_group(ms_, x):
+        nwc.matvec_group([m["dm"] for m in ms_], [x] * len(ms_), [m["y"] for m in ms_])
+        return [m["y"] for m in ms_]
+
+    # The step as the headline of this workload: q,k,v and gate,up each one
+    # grouped launch (separately encoded matrices), 4 launches per layer.
+    g_step = graph_of(lambda: qwen25_step(torch, stack, head, h0, nwc_linear, group=nwc_group))
     ms = time_region(torch, g_step.replay, args.steps, args.warmup)
+    g_7 = graph_of(lambda: qwen25_step(torch, stack, head, h0, nwc_linear))
+    ms_7 = time_region(torch, g_7.replay, args.steps, args.warmup)
     xs = {id(m): torch.zeros(m["k"], dtype=torch.bfloat16, device=dev) for m in mats}
     g_mv = graph_of(lambda: [m["dm"].matvec(xs[id(m)], m["y"]) for m in mats])
     ms_mv = time_region(torch, g_mv.replay, args.steps, args.warmup)
@@ -258,8 +272,11 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
            "ms_matvecs_only": round(ms_mv, 4), "ms_glue": round(ms - ms_mv, 4),
            "compressed_GBps_matvecs": round(algo / (ms_mv * 1e-3) / 1e9, 1),
            "compressed_GB": round(algo / 1e9, 4), "blob_GB": round(sum(m["blob_bytes"] for m in mats) / 1e9, 4),
+           "launches": "q,k,v one nwc_matvec_group launch, o, gate,up one launch, down; lm_head",
+           "one_launch_per_matrix": {"ms_per_step": round(ms_7, 4), "tokens_per_s": round(1e3 / ms_7, 2)},
            "fused_projections": {"ms_per_step": round(ms_fused, 4), "tokens_per_s": round(1e3 / ms_fused, 2),
-                                 "note": "q||k||v and gate||up each one matrix (one launch), 4 launches per layer"},
+                                 "note": "q||k||v and gate||up each encoded as one matrix (one launch), "
+                                         "4 launches per layer"},
            "timing": "HIP graph replay of the whole step (glue in torch); matvecs alone in a second graph",
            "kernel_source_hash": kernel_source_hash()}
     if not args.no_bf16_baseline:
@@ -273,6 +290,23 @@ def bench_qwen25_step(args, torch, nwc, S, C, dev):
                                 "speedup_compressed_vs_bf16": round(ms_bf / ms, 4),
                                 "logits_rel_l2_vs_bf16_stack": rel,
                                 "kernel": "torch.nn.functional.linear (hipBLASLt/rocBLAS), same glue"}
+        # The library's plain BF16 GEMV with the same launch structure (grouped q,k,v and gate,up).
+        for m in mats:
+            m["y_plain"] = torch.empty(m["n"], dtype=torch.float32, device=dev)
+
+        def plain_linear(m, x):
+            nwc.bf16_gemv(m["w_bf16"], x, m["y_plain"])
+            return m["y_plain"]
+
+        def plain_group(ms_, x):
+            nwc.bf16_gemv_group([m["w_bf16"] for m in ms_], [x] * len(ms_), [m["y_plain"] for m in ms_])
+            return [m["y_plain"] for m in ms_]
+
+        g_pl = graph_of(lambda: qwen25_step(torch, stack, head, h0, plain_linear, group=plain_group))
+        ms_pl = time_region(torch, g_pl.replay, args.steps, args.warmup)
+        out["bf16_plain_gemv_grouped"] = {"ms_per_step": round(ms_pl, 4), "tokens_per_s": round(1e3 / ms_pl, 2),
+                                          "speedup_compressed_vs_plain": round(ms_pl / ms, 4),
+                                          "kernel": "nwc_bf16_gemv_group / nwc_bf16_gemv, same launch structure"}
     print(json.dumps(out), flush=True)
 
 
@@ -494,14 +528,14 @@ def summarize_traffic(fetch_csv, write_csv, profile_json, cmd_fetch, cmd_write):
     res = {}
     for cname, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == cname]
-        first_mv = min(int(r["Dispatch_Id"]) for r in rows if "matvec_kernel" in r["Kernel_Name"])
+        first_mv = min(int(r["Dispatch_Id"]) for r in rows if "matvec" in r["Kernel_Name"])
         copies = [r for r in rows if int(r["Dispatch_Id"]) < first_mv and "copy" in r["Kernel_Name"].lower()]
         cal = max(float(r["Counter_Value"]) for r in copies)
-        mv = [float(r["Counter_Value"]) for r in rows if "matvec_kernel" in r["Kernel_Name"]]
+        mv = [float(r["Counter_Value"]) for r in rows if "matvec" in r["Kernel_Name"]]
         res[cname] = {"scale": true_kib / cal, "cal_kib": cal, "dispatches": len(mv),
                       "mean_kib": statistics.mean(mv), "bytes": statistics.mean(mv) * 1024 * true_kib / cal}
     hbm = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
-    algo, blob = meta["algo_bytes_per_matvec"], meta["blob_bytes_per_matvec"]
+    algo, blob = meta["algo_bytes_per_launch"], meta["blob_bytes_per_launch"]
     d = {"kernel_source_hash": meta["kernel_source_hash"], "hbm_bytes_per_launch": round(hbm, 1),
          "fetch_bytes_per_launch": round(res["FETCH_SIZE"]["bytes"], 1),
          "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes"], 1),
@@ -510,7 +544,7 @@ def summarize_traffic(fetch_csv, write_csv, profile_json, cmd_fetch, cmd_write):
          "dispatches": res["FETCH_SIZE"]["dispatches"]}
     json.dump(d, open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.json"), "w"), indent=1)
     with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_traffic.md"), "w") as f:
-        f.write("# matvec kernel HBM traffic, Qwen3-4B layer set (252 matvecs), MI355X\n\n"
+        f.write("# matvec kernel HBM traffic, Qwen3-4B layer set (252 matvecs in 144 launches per step), MI355X\n\n"
                 "Commands (from the repository root on an MI355X machine, with `TMPDIR=/tmp`):\n\n"
                 f"    {cmd_fetch}\n    {cmd_write}\n\nSummarised with `python bench.py --summarize-traffic` "
                 "(the counter CSVs and the JSON line the profiled run printed).\n\n"
@@ -523,40 +557,47 @@ def summarize_traffic(fetch_csv, write_csv, profile_json, cmd_fetch, cmd_write):
             r = res[cname]
             f.write(f"| {cname} | {r['cal_kib']:.0f} | {true_kib:.0f} | {r['scale']:.3f} | {r['dispatches']} | "
                     f"{r['mean_kib']:.1f} | {r['bytes']:.0f} |\n")
-        f.write(f"\nPer matvec (mean over the layer set): HBM traffic {hbm / 1e6:.3f} MB; algorithmic bytes "
-                f"(coded bits/8 + 2K + 4N) {algo / 1e6:.3f} MB; blob bytes {blob / 1e6:.3f} MB.\n"
+        f.write(f"\nPer launch (mean over the step's launches: q,k,v group, o, gate,up group, down): HBM traffic "
+                f"{hbm / 1e6:.3f} MB; algorithmic bytes "
+                f"(coded bits/8 + 2K + 4N per matrix) {algo / 1e6:.3f} MB; blob bytes {blob / 1e6:.3f} MB.\n"
                 f"Traffic / algorithmic = {hbm / algo:.3f}; traffic / blob = {hbm / blob:.3f}.\n")
     print(json.dumps(d, indent=1))
 
 
 def summarize_counters(csv_path, profile_json, cmd):
-    """One counter run of `--profile-sweeps N` with SQ/GRBM counters -> instructions and clocks per 64 weights."""
+    """One counter run of `--profile-sweeps N` with SQ counters -> instructions per 64 weights.
+
+    Only instruction counts are reported: the counters are collected with the
+    dispatches serialized, so cycle counters there do not describe the timed step."""
     import collections
     import csv
     import statistics
     meta = json.loads(open(profile_json).read().strip().splitlines()[-1])
     per = collections.defaultdict(list)
     for r in csv.DictReader(open(csv_path)):
-        if "matvec_kernel" in r["Kernel_Name"]:
+        if "matvec" in r["Kernel_Name"]:
             per[r["Counter_Name"]].append(float(r["Counter_Value"]))
     mean = {c: statistics.mean(v) for c, v in per.items()}
-    w64 = meta["weights_per_matvec"] / 64.0
+    w64 = meta["weights_per_launch"] / 64.0
     derived = {}
     if "SQ_INSTS_VALU" in mean:
         derived["VALU instructions per 64 weights (wave-level)"] = mean["SQ_INSTS_VALU"] / w64
     if "SQ_INSTS_LDS" in mean:
         derived["LDS instructions per 64 weights"] = mean["SQ_INSTS_LDS"] / w64
+    if "SQ_INSTS_SALU" in mean:
+        derived["SALU instructions per 64 weights"] = mean["SQ_INSTS_SALU"] / w64
+    if "SQ_INSTS_VMEM_RD" in mean:
+        derived["vector memory reads per 64 weights"] = mean["SQ_INSTS_VMEM_RD"] / w64
     if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean:
         derived["LDS bank-conflict cycles / LDS active cycles"] = mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"]
-    if "GRBM_GUI_ACTIVE" in mean:
-        derived["GRBM_GUI_ACTIVE per matvec"] = mean["GRBM_GUI_ACTIVE"]
     with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_counters.md"), "w") as f:
-        f.write("# matvec kernel instruction and LDS counters, Qwen3-4B layer set (252 matvecs), MI355X\n\n"
+        f.write("# matvec kernel instruction and LDS counters, Qwen3-4B layer set (144 launches per step), MI355X\n\n"
                 "Command (from the repository root on an MI355X machine, with `TMPDIR=/tmp`):\n\n"
                 f"    {cmd}\n\nSummarised with `python bench.py --summarize-counters`.\n\n"
                 f"Kernel source hash: {meta['kernel_source_hash']}\n\n"
-                f"Mean per matvec dispatch ({len(next(iter(per.values())))} dispatches, "
-                f"{meta['weights_per_matvec'] / 1e6:.2f} M weights each on average):\n\n"
+                f"Mean per matvec launch ({len(next(iter(per.values())))} dispatches, "
+                f"{meta['weights_per_launch'] / 1e6:.2f} M weights each on average).  Counter runs serialize the "
+                "dispatches, so only instruction counts (not cycle counts) are used:\n\n"
                 "| counter | mean per dispatch |\n|---|---|\n")
         for c in sorted(mean):
             f.write(f"| {c} | {mean[c]:.4g} |\n")
@@ -577,17 +618,24 @@ def summarize_workload(run_json, cmd):
         body = ("# Qwen2.5-7B-shaped batch-1 decode step, MI355X\n\n"
                 f"Command (from the repository root on an MI355X machine):\n\n    {cmd}\n\n"
                 "28 layers x {q 3584x3584, k/v 512x3584, o 3584x3584, gate/up 18944x3584, down 3584x18944} + lm_head\n"
-                "152064x3584, N(0, 1/sqrt(K)); every linear through `nwc_matvec`; glue in torch (RMS norms with unit\n"
+                "152064x3584, N(0, 1/sqrt(K)); every linear through the library (q,k,v and gate,up grouped); glue in torch (RMS norms with unit\n"
                 "weight, fp32 residual, context-1 attention stand-in = v repeated over the GQA heads, silu(gate)*up).\n"
                 "The same step with `torch.nn.functional.linear` on the BF16 weights is the baseline.\n\n"
                 "| | ms per token | tokens/s |\n|---|---|---|\n"
-                f"| nwc_matvec step, 7 launches per layer (graph replay) | {d['ms_per_step']} | {d['value']} |\n"
-                f"| of which the {d['config']['matrices']} matvecs alone | {d['ms_matvecs_only']} | — |\n")
+                f"| nwc step, q,k,v and gate,up grouped (4 launches per layer, graph replay) | {d['ms_per_step']} | "
+                f"{d['value']} |\n"
+                f"| nwc step, one launch per matrix (7 per layer) | {d['one_launch_per_matrix']['ms_per_step']} | "
+                f"{d['one_launch_per_matrix']['tokens_per_s']} |\n"
+                f"| the {d['config']['matrices']} matvecs alone, one launch each | {d['ms_matvecs_only']} | — |\n")
         if f_:
             body += (f"| nwc_matvec step, q\\|\\|k\\|\\|v and gate\\|\\|up fused (4 launches per layer) | "
                      f"{f_['ms_per_step']} | {f_['tokens_per_s']} |\n")
         if b:
             body += f"| BF16 `F.linear` step, same glue | {b['ms_per_step']} | {b['tokens_per_s']} |\n"
+        p_ = d.get("bf16_plain_gemv_grouped")
+        if p_:
+            body += (f"| plain BF16 GEMV step (library's `nwc_bf16_gemv`, grouped like the headline) | "
+                     f"{p_['ms_per_step']} | {p_['tokens_per_s']} |\n")
         body += (f"\nMatvecs {d['compressed_GBps_matvecs']} GB/s on {d['compressed_GB']} GB of algorithmic bytes "
                  f"({d['blob_GB']} GB of blobs)")
         if b:
@@ -605,9 +653,11 @@ def summarize_workload(run_json, cmd):
                 f"| gather of 4096 ids, nwc_gather | {d['gather_4096']['us']} | torch index_select on the BF16 table: "
                 f"{d['gather_4096']['torch_index_select_on_bf16_us']} us |\n"
                 f"| dequantize the whole matrix | {d['dequant_full']['us']} | {d['dequant_full']['GBps_written']} GB/s written |\n")
-        for k, v in fp8.items():
-            body += (f"| fp8 matvec {k} (rotation over {v['rotation']}) | {v['us']} | {v['compressed_GBps']} GB/s, "
-                     f"{v['bits_per_weight_coded']} coded bits/weight |\n")
+        for k, byc in fp8.items():
+            for cname, v in byc.items():
+                body += (f"| fp8 matvec {k}, {cname} coder (rotation over {v['rotation']}) | {v['us']} | "
+                         f"{v['compressed_GBps']} GB/s, {v['bits_per_weight_coded']} coded bits/weight, "
+                         f"{v['bits_per_weight_blob']} blob bits/weight |\n")
         body += ("\nThe 1024x1024 matrices (BF16 and fp8) fit in cache: their times are latency figures, not bandwidth "
                  f"claims.\nKernel source hash {d['kernel_source_hash']}.\n")
     elif wl == "prefill":
@@ -627,44 +677,74 @@ def summarize_workload(run_json, cmd):
         f.write(body + "\n```\n" + json.dumps(d) + "\n```\n")
 
 
-def summarize_trace(prof_dir, bench_json, cmd):
-    """Kernel-trace run of the layer set -> per-kernel and per-launch-shape durations."""
+def summarize_trace(prof_dir, profile_json, bench_json, cmd):
+    """Kernel trace of `--profile-sweeps N` (the timed step's graph, replayed N times) -> per-launch-kind
+    durations, their sum per step against the bench's ms_per_step, and the dominant kernel's bytes/time."""
     import collections
     import csv
     import statistics
-    stats = list(csv.DictReader(open(os.path.join(prof_dir, "run_kernel_stats.csv"))))
-    trace = list(csv.DictReader(open(os.path.join(prof_dir, "run_kernel_trace.csv"))))
+    import glob
+
+    def find(name):
+        hits = sorted(glob.glob(os.path.join(prof_dir, "**", name), recursive=True))
+        if not hits:
+            raise SystemExit(f"{name} not found under {prof_dir}")
+        return hits[0]
+
+    trace = list(csv.DictReader(open(find("run_kernel_trace.csv"))))
+    stats = list(csv.DictReader(open(find("run_kernel_stats.csv"))))
+    meta = json.loads(open(profile_json).read().strip().splitlines()[-1])
     d = json.loads(open(bench_json).read().strip().splitlines()[-1])
-    by = collections.defaultdict(list)
-    for r in trace:
-        if "matvec_kernel" in r["Kernel_Name"]:
-            key = (_short_kernel(r["Kernel_Name"]), r.get("Grid_Size") or r.get("Grid_Size_X"),
-                   r.get("Workgroup_Size") or r.get("Workgroup_Size_X"))
-            by[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    mv = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if "matvec_kernel" in r["Kernel_Name"]]
+    mv = [r for r in trace if "matvec" in r["Kernel_Name"]]
+    mv.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per_sweep = meta["launches_per_sweep"]
+    kinds = list(meta["per_launch_kind"])
+    assert len(mv) == meta["profile_sweeps"] * per_sweep, (len(mv), meta["profile_sweeps"], per_sweep)
+    # Dispatch i of a sweep is launch kind i % 4 (layer order q,k,v | o | gate,up | down).
+    dur = collections.defaultdict(list)
+    for i, r in enumerate(mv):
+        dur[kinds[(i % per_sweep) % len(kinds)]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    layers = meta["layers"]
+    step_from_medians = sum(statistics.median(v) for v in dur.values()) * layers / 1e6  # ms
+    mean_all = statistics.mean(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mv)
+    sweeps = [mv[j * per_sweep:(j + 1) * per_sweep] for j in range(meta["profile_sweeps"])]
+    span = [(int(s[-1]["End_Timestamp"]) - int(s[0]["Start_Timestamp"])) / 1e6 for s in sweeps]
+    algo_launch = meta["algo_bytes_per_launch"]
     with open(os.path.join(ROOT, "profiles", "matvec_qwen3_4b_kernel_trace.md"), "w") as f:
-        f.write("# matvec kernel trace -- Qwen3-4B layer set (36 layers x 7 matrices), MI355X\n\n"
+        f.write("# matvec kernel trace -- Qwen3-4B layer set, the timed step only, MI355X\n\n"
                 "Command (from the repository root on an MI355X machine, with `TMPDIR=/tmp`):\n\n"
-                f"    {cmd}\n\nSummarised with `python bench.py --summarize-trace`.\n\n"
-                f"Kernel source hash: {d['kernel_source_hash']}\n\n"
-                "`run_kernel_stats.csv`, matvec rows (copy and `at::native` kernels are input set-up outside "
-                "the timed region):\n\n| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n")
+                f"    {cmd}\n\nSummarised with `python bench.py --summarize-trace` from that run's CSVs and JSON "
+                "line and the JSON line of a plain `python bench.py` run of the same source.\n\n"
+                f"Kernel source hash: {meta['kernel_source_hash']} (bench run: {d['kernel_source_hash']})\n\n"
+                f"The profiled run replays the step's HIP graph {meta['profile_sweeps']} times; the trace holds "
+                f"exactly {len(mv)} matvec dispatches = {meta['profile_sweeps']} x {per_sweep} (36 layers x "
+                "{q,k,v group, o, gate,up group, down}); nothing else runs between them.\n\n"
+                "| launch kind | matrices | dispatches | median us | mean us | algorithmic MB | GB/s at the median |\n"
+                "|---|---|---|---|---|---|---|\n")
+        for k in kinds:
+            v = dur[k]
+            info = meta["per_launch_kind"][k]
+            med = statistics.median(v) / 1e3
+            f.write(f"| {k} | {'+'.join(info['matrices'])} | {len(v)} | {med:.2f} | {statistics.mean(v) / 1e3:.2f} | "
+                    f"{info['algo_bytes'] / 1e6:.2f} | {info['algo_bytes'] / (med * 1e-6) / 1e9:.0f} |\n")
+        f.write("\n| | ms per step |\n|---|---|\n"
+                f"| sum of the per-kind medians x {layers} layers (kernel execution only) | {step_from_medians:.4f} |\n"
+                f"| first-to-last dispatch span of one replay under the profiler (median of {len(span)}) | "
+                f"{statistics.median(span):.4f} |\n"
+                f"| bench.py `ms_per_step` (HIP events around graph replays, no profiler) | {d['ms_per_step']} |\n\n"
+                f"All {len(mv)} matvec dispatches: mean {mean_all / 1e3:.3f} us.  Dominant kernel (the fused decode + "
+                f"matvec, both entry points): {algo_launch / 1e6:.3f} MB algorithmic per launch / {mean_all / 1e3:.3f} us "
+                f"= {algo_launch / (mean_all * 1e-9) / 1e9:.0f} GB/s "
+                f"({algo_launch / (mean_all * 1e-9) / 1e9 / HBM_PEAK_GBPS:.4f} of 8 TB/s) from the trace; the bench "
+                f"line's roofline gives {d['roofline']['achieved']} GB/s ({d['roofline']['frac']}) with launch gaps "
+                "counted.\n\n`run_kernel_stats.csv`, matvec rows:\n\n"
+                "| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n")
         for r in stats:
-            if "matvec_kernel" in r["Name"] or "reduce_kernel" in r["Name"]:
+            if "matvec" in r["Name"]:
                 f.write(f"| {_short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |\n")
-        f.write(f"\nAll matvec dispatches: {len(mv)}, mean {statistics.mean(mv) / 1e3:.3f} us (kernel execution "
-                "only; the bench's HIP events also count the gaps between graph nodes).\n\n"
-                "Per launch shape from `run_kernel_trace.csv` (grid = threads; template arguments "
-                "<fp8, 16-column groups per lane, split rows>):\n\n"
-                "| kernel | grid | block | dispatches | median us | mean us |\n|---|---|---|---|---|---|\n")
-        for (nm, gs, ws), v in sorted(by.items(), key=lambda kv: -statistics.mean(kv[1])):
-            f.write(f"| {nm} | {gs} | {ws} | {len(v)} | {statistics.median(v) / 1e3:.2f} | {statistics.mean(v) / 1e3:.2f} |\n")
-        keep = {k: d.get(k) for k in ("value", "unit", "ms_per_step", "us_per_layer", "us_per_matvec_avg",
-                                      "roofline", "cpu_baseline", "bf16_baseline")}
-        keep["per_shape_us"] = {k: v["us"] for k, v in d["per_shape"].items()}
-        f.write("\nThe JSON line of the profiled run (its HIP events time the graph-replayed sweep, launch gaps "
-                f"included: {d['us_per_matvec_avg']:.2f} us per matvec):\n\n```\n{json.dumps(keep)}\n```\n")
+        keep = {k: d.get(k) for k in ("value", "unit", "ms_per_step", "us_per_layer", "roofline")}
+        f.write(f"\nThe bench line (abridged):\n\n```\n{json.dumps(keep)}\n```\n")
 
 
 def main():
@@ -685,7 +765,7 @@ def main():
                          "size for scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--summarize-traffic", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "RUN_JSON", "CMD_F", "CMD_W"),
                     help="write profiles/matvec_qwen3_4b_traffic.{json,md} from two counter runs and exit")
-    ap.add_argument("--summarize-trace", nargs=3, metavar=("PROF_DIR", "RUN_JSON", "CMD"),
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("PROF_DIR", "PROFILE_JSON", "BENCH_JSON", "CMD"),
                     help="write profiles/matvec_qwen3_4b_kernel_trace.md from a kernel-trace run and exit")
     ap.add_argument("--summarize-workload", nargs=2, metavar=("RUN_JSON", "CMD"),
                     help="write the profiles/ summary of a qwen25_7b_step, tied_embedding or prefill run and exit")
@@ -759,12 +839,13 @@ def main():
             dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
-        # The timed step's launches only: the sweep captured once and replayed.
+        # The timed step's launches only: the sweep captured once (capture
+        # launches nothing) and replayed N times, so a kernel trace holds
+        # exactly N x launches_per_sweep matvec dispatches.
         pg = torch.cuda.CUDAGraph()
-        sweep()
-        torch.cuda.synchronize()
         with torch.cuda.graph(pg):
             sweep()
+        torch.cuda.synchronize()
         for _ in range(args.profile_sweeps):
             pg.replay()
         torch.cuda.synchronize()
@@ -773,8 +854,12 @@ def main():
                           "algo_bytes_per_launch": sum(m["algo_bytes"] for m in mats) / n_launch,
                           "blob_bytes_per_launch": sum(m["blob_bytes"] for m in mats) / n_launch,
                           "weights_per_launch": sum(m["n"] * m["k"] for m in mats) / n_launch,
-                          "per_group_algo_bytes": {gname: sum(m["algo_bytes"] for m in launch_groups[i])
-                                                   for i, (gname, _) in enumerate(FUSED_QWEN3)},
+                          "per_launch_kind": {gname: {"matrices": list(parts),
+                                                      "algo_bytes": sum(m["algo_bytes"] for m in launch_groups[i]),
+                                                      "blob_bytes": sum(m["blob_bytes"] for m in launch_groups[i]),
+                                                      "weights": sum(m["n"] * m["k"] for m in launch_groups[i])}
+                                              for i, (gname, parts) in enumerate(FUSED_QWEN3)},
+                          "layers": args.layers,
                           "copy_calibration_bytes": (64 << 20) * 4 if args.copy_calibration else 0,
                           "kernel_source_hash": kernel_source_hash()}), flush=True)
         return

@@ -55,7 +55,7 @@ def traffic_from_profiles(algo_bytes_per_launch: float):
 FUSED_QWEN3 = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
 
 
-def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16, fused=False):
+def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16, fused=False, cols=0, rows=0):
     """The Qwen3-4B layer set, one compressed matrix per projection; with `fused`,
     also the projections that share an input in a decoder layer encoded as one
     matrix each (q||k||v and gate||up rows concatenated, one rank table), whose
@@ -68,7 +68,7 @@ def build_layer_set(torch, nwc, S, C, dev, layers, with_bf16, fused=False):
             ws, xs = C.qwen3_seed(layer, idx)
             w = S.blocked_normal_bf16(ws, (n, k), np.float32(C.sigma_for(k)))
             wt = torch.from_numpy(w.view(np.int16)).to(dev).view(torch.bfloat16) if with_bf16 else None
-            blob = nwc.encode(w)
+            blob = nwc.encode(w, cols_per_lane=cols, rows_per_wave=rows)
             dm = nwc.DeviceMatrix(blob, dev)
             x = S.activation_bf16(xs, k)
             xd = torch.from_numpy(x.view(np.int16)).to(dev)
@@ -357,6 +357,62 @@ def bench_prefill(args, torch, nwc, S, C, dev):
            "data": "synthetic (seeded N(0,1/sqrt(K)) BF16 weights)",
            "config": {"workload": "prefill", "layers": layers, "tokens": [16, 128, 512]},
            "per_tokens": rows, "kernel_source_hash": kernel_source_hash()}
+    print(json.dumps(out), flush=True)
+
+
+def bench_small_batch(args, torch, nwc, S, C, dev):
+    """A few tokens at once on the Qwen3-4B layer matrices (12 layers in rotation: 1.85 GB of blobs, 2.4 GB
+    of BF16, far beyond the last-level cache): nwc_matvec (B = 1) and the VALU batch path (B = 4) on the
+    default encodings; the matrix-core path (B = 8, 16, 32) on encodings of 16 rows per wave; against
+    torch.nn.functional.linear (hipBLASLt) on the BF16 weights with the same B."""
+    F = torch.nn.functional
+    layers = args.layers or 12
+    mats, _ = build_layer_set(torch, nwc, S, C, dev, layers, True)
+    mats16, _ = build_layer_set(torch, nwc, S, C, dev, layers, False, cols=16, rows=16)
+    algo = sum(m["algo_bytes"] for m in mats)
+    rows = {}
+    for B in (1, 4, 8, 16, 32):
+        ks = {m["k"] for m in mats}
+        xs = {k: torch.from_numpy(np.stack([S.activation_bf16(9000 + t, k) for t in range(B)]).view(np.int16))
+              .to(dev) for k in ks}
+        ys = [torch.empty((B, m["n"]), dtype=torch.float32, device=dev) for m in mats]
+        use = mats if B < 5 else mats16
+
+        def nwc_pass():
+            for m, y in zip(use, ys):
+                if B == 1:
+                    m["dm"].matvec(xs[m["k"]][0], y[0])
+                else:
+                    m["dm"].matvec_batch(xs[m["k"]], y)
+
+        def bf16_pass():
+            for m in mats:
+                F.linear(xs[m["k"]].view(torch.bfloat16), m["w_bf16"])
+
+        res = {}
+        for tag, fn in (("nwc", nwc_pass), ("bf16", bf16_pass)):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            res[tag] = time_region(torch, g.replay, args.steps, args.warmup) * 1e3 / layers  # us per layer
+        path = "nwc_matvec" if B == 1 else "VALU batch (nwc_matvec_batch)" if B < 5 else \
+            "matrix cores (nwc_matvec_batch, 16 rows per wave)"
+        rows[str(B)] = {"path": path, "us_per_layer_nwc": round(res["nwc"], 2),
+                        "us_per_token_layer_nwc": round(res["nwc"] / B, 2),
+                        "us_per_layer_bf16_F_linear": round(res["bf16"], 2),
+                        "nwc_speedup_vs_bf16": round(res["bf16"] / res["nwc"], 3),
+                        "compressed_GBps_nwc": round(algo / layers / (res["nwc"] * 1e-6) / 1e9, 1)}
+        log(f"[bench] small batch B={B}: {rows[str(B)]}")
+    out = {"metric": "small batches on the Qwen3-4B layer matrices: us per layer, nwc vs BF16 F.linear",
+           "value": rows["32"]["us_per_token_layer_nwc"], "unit": "us per token-layer (B=32)", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(rows["32"]["us_per_layer_nwc"] * layers / 1e3, 4), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1/sqrt(K)) BF16 weights)",
+           "config": {"workload": "small_batch", "layers": layers, "batches": [1, 4, 8, 16, 32]},
+           "per_batch": rows, "kernel_source_hash": kernel_source_hash()}
     print(json.dumps(out), flush=True)
 
 
@@ -671,6 +727,17 @@ def summarize_workload(run_json, cmd):
             body += (f"| {t} | {r['us_per_layer_nwc']} | {r['us_per_layer_bf16']} | {r['us_per_layer_dequant']} | "
                      f"{r['nwc_over_bf16']} |\n")
         body += f"\nKernel source hash {d['kernel_source_hash']}.\n"
+    elif wl == "small_batch":
+        path = os.path.join(ROOT, "profiles", "small_batch_qwen3_4b.md")
+        body = ("# Small batches on the Qwen3-4B layer matrices, MI355X\n\n"
+                f"Command (from the repository root on an MI355X machine):\n\n    {cmd}\n\n"
+                f"{d['config']['layers']} layers x 7 matrices in rotation (cold); B activation rows per matrix; "
+                "HIP-graph replay.\n\n| B | path | us per layer | us per token-layer | BF16 `F.linear` us per layer "
+                "| nwc speed-up | compressed GB/s |\n|---|---|---|---|---|---|---|\n")
+        for b, r in d["per_batch"].items():
+            body += (f"| {b} | {r['path']} | {r['us_per_layer_nwc']} | {r['us_per_token_layer_nwc']} | "
+                     f"{r['us_per_layer_bf16_F_linear']} | {r['nwc_speedup_vs_bf16']} | {r['compressed_GBps_nwc']} |\n")
+        body += f"\nKernel source hash {d['kernel_source_hash']}.\n"
     else:
         raise SystemExit(f"no summary for workload {wl}")
     with open(path, "w") as f:
@@ -752,7 +819,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step", "tied_embedding", "prefill"),
+    ap.add_argument("--workload", choices=("qwen3_4b_layer_set", "qwen25_7b_step", "tied_embedding", "prefill",
+                                           "small_batch"),
                     default="qwen3_4b_layer_set")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -804,6 +872,9 @@ def main():
         return
     if args.workload == "prefill":
         bench_prefill(args, torch, nwc, S, C, dev)
+        return
+    if args.workload == "small_batch":
+        bench_small_batch(args, torch, nwc, S, C, dev)
         return
     args.layers = args.layers or C.QWEN3_4B_LAYERS
     mats, fmats = build_layer_set(torch, nwc, S, C, dev, args.layers,

@@ -311,14 +311,14 @@ __device__ __forceinline__ void fetch_code_ahead(const uint8_t *code, uint32_t o
 template <int PR>
 __device__ __forceinline__ void commit_code_ahead(const uint8_t *code, uint32_t off, uint32_t rows,
                                                   uint32_t region_rows, uint32_t region, uint32_t lane,
-                                                  const uint32_t (&w)[PR]) {
+                                                  const uint32_t (&w)[PR], uint32_t col) {
 #pragma unroll
   for (int j = 0; j < PR; ++j)
-    if ((uint32_t)j < region_rows) lds_store(region + j * 256 + 4 * lane, w[j]);
+    if ((uint32_t)j < region_rows) lds_store(region + j * 256 + 4 * col, w[j]);
   if (rows + NWC_GUARD_ROWS > (uint32_t)PR) {
     if (rows > (uint32_t)PR) dma_to_lds(code + off + PR * 256, region + PR * 256, (rows - PR) * 256, lane);
-    lds_store(region + rows * 256 + 4 * lane, 0u);
-    lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
+    lds_store(region + rows * 256 + 4 * col, 0u);
+    lds_store(region + (rows + 1) * 256 + 4 * col, 0u);
     wait_vm0();
   }
 }
@@ -591,7 +591,7 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
     uint32_t cur[kWinMax];
 #pragma unroll
     for (uint32_t j = 0; j < kWinMax; ++j) cur[j] = ahead[j];
-    if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead);
+    if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead, lane);
     // Mantissas of this item, then the next item's code rows: the decode below
     // needs neither, so both stream in while it runs (the compiler waits for
     // the mantissas at the multiply-adds, which it places after the decode
@@ -933,7 +933,7 @@ __global__ __launch_bounds__(1024) void dequant_kernel(Geom g, const uint32_t *_
     uint32_t cur[kWinMax];
 #pragma unroll
     for (uint32_t j = 0; j < kWinMax; ++j) cur[j] = ahead[j];
-    if (wn == 0) commit_code_ahead<PR>(code, items[2 * pl.item], rows, region_rows, region, lane, ahead);
+    if (wn == 0) commit_code_ahead<PR>(code, items[2 * pl.item], rows, region_rows, region, lane, ahead, lane);
     uint4 m[NG];
     if (!FP8) {
       const uint4 *mp = mant_base(g, pl.item, lane);
@@ -981,6 +981,182 @@ __global__ __launch_bounds__(1024) void dequant_kernel(Geom g, const uint32_t *_
     }
   }
   flush();
+}
+
+// ----------------------------------------------------------------- matrix-core small batches
+// y_b = W x_b for a batch of up to 32 activation rows, each weight decoded
+// once and multiplied on the matrix cores (v_mfma_f32_16x16x32_bf16), for
+// BF16 blobs of 16 rows per work item (S = 4 slices of C = 16 or 32 columns
+// per row).
+//
+// The matrix-core product sums over its 32-long k index in any order, so only
+// A and B have to agree on which column each k stands for.  Lane l decodes the
+// stream of the item's lane 4 (l % 16) + l / 16, i.e. row l % 16 and slice
+// l / 16; every 8 decoded columns of its slice are then, as they come out of
+// the decoder, lane l's A operand of one product (row l % 16, k = 8 (l/16) +
+// i), and B is the same 8 columns of x for token l % 16: one 16-byte load.
+// No tile, no LDS round trip: D (16 rows x 16 tokens, fp32; lane l holds rows
+// 4 (l/16) .. +4 of token l % 16) accumulates over the item's 2C/16 products.
+// Lane layouts checked on MI355X with an in-bounds probe.
+//
+// A workgroup of W waves (the blob's waves per group) owns one row group at a
+// time, persistent over row groups; wave w takes the items (row group, span,
+// w) of every span, so the waves split the columns as in the matvec.  At the
+// end of a row group each wave leaves its D in its slot of one of two partial
+// buffers (alternating by row group), and after one barrier the workgroup sums
+// the W partials of each output in wave order (a fixed order: repeated calls
+// give identical bits) and stores it.  Two buffers: a wave writes a row
+// group's partials only after the barrier that ends the previous row group,
+// which every thread reaches after its sums over the buffer before.
+struct MfmaArgs {
+  const uint8_t *mant;
+  uint32_t n, k, ldx, ldy, batch, region_words, r2s_lo, r2s_hi, n_spans;
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) float lds_f32;
+
+constexpr uint32_t kMfmaPartBytes = 4 * 64 * 4;  // one wave's D for 16 tokens
+
+template <int NG, int NH>
+__global__ __launch_bounds__(1024) void matvec_mfma_kernel(const uint32_t *__restrict__ items,
+                                                           const uint8_t *__restrict__ code,
+                                                           const uint8_t *__restrict__ lut,
+                                                           const uint16_t *__restrict__ x, uint32_t n_groups,
+                                                           uint32_t W, const MfmaArgs a, float *__restrict__ y) {
+  constexpr uint32_t C = 16 * NG;
+  constexpr int PR = 2 * NG + 2;
+  constexpr uint32_t kWinMax = 4;
+  constexpr uint32_t kPart = NH * kMfmaPartBytes;
+  __shared__ uint32_t s_lut[NWC_LUT_ENTRIES];
+  extern __shared__ uint32_t s_dyn[];
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t src = 4u * (lane & 15u) + (lane >> 4);  // the item lane whose stream this lane decodes
+  const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;
+  const uint32_t region_rows = a.region_words >> 6;
+  const uint32_t parts = lds_addr(s_dyn) + W * a.region_words * 4;  // [2][W] x kPart bytes
+  const uint32_t lut_lds = lds_addr(s_lut);
+  const uint32_t grid = gridDim.x, first = blockIdx.x;
+  const uint32_t n_mine = (n_groups - first + grid - 1) / grid;  // grid <= n_groups
+  const uint32_t total = n_mine * a.n_spans;                     // items of this wave
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, (int)(a.batch * a.ldx * 2u), kBufWord3);
+  for (uint32_t p = wave; p < NWC_LUT_BYTES / 1024; p += W) dma_1k(lut + p * 1024, lut_lds + p * 1024, 1024, lane);
+  uint32_t ahead[PR];
+  {
+    const uint32_t it0 = first * a.n_spans * W + wave;
+    fetch_code_ahead<PR>(code, items[2 * it0], items[2 * it0 + 1], src, ahead);
+  }
+  wait_vm0();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+
+  floatx4_t acc[NH];
+  uint32_t rg = first, sp = 0, parity = 0;
+  for (uint32_t t = 0; t < total; ++t) {
+    const uint32_t item = (rg * a.n_spans + sp) * W + wave;
+    if (sp == 0) {
+#pragma unroll
+      for (int h = 0; h < NH; ++h) acc[h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const uint32_t rows = items[2 * item + 1];
+    const uint32_t wn = rows > kWinMax ? 0u : rows < 2u ? 2u : rows;
+    uint32_t cur[kWinMax];
+#pragma unroll
+    for (uint32_t q = 0; q < kWinMax; ++q) cur[q] = ahead[q];
+    if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead, src);
+    // This item's mantissas and activation columns, then the next item's code
+    // rows (the decode waits for the code rows fetched one item earlier, the
+    // products for the first two).  The activations are buffer loads over the
+    // batch's rows: a token past the batch (offset past the buffer) or a
+    // column block past k (offset forced past it) reads zeros, with no select
+    // after the load (one would wait for the data right there).
+    const uint32_t c0 = ((sp * W + wave) * 4 + (lane >> 4)) * C;  // first column of this lane's slice
+    uint4 m[NG];
+    {
+      const uint4 *mp = (const uint4 *)(a.mant + (uint64_t)item * (64 * C)) + src;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) m[q] = mp[q * 64];
+    }
+    u32x4_t xf[2 * NG][NH];
+#pragma unroll
+    for (int kb = 0; kb < 2 * NG; ++kb)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t tok = h * 16 + (lane & 15u), col = c0 + 8 * kb;
+        const uint32_t off = col < a.k ? (tok * a.ldx + col) * 2u : 0x80000000u;
+        xf[kb][h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      }
+    {
+      const bool more = t + 1 < total;
+      const uint32_t nx = sp + 1 < a.n_spans ? item + W : ((rg + grid) * a.n_spans) * W + wave;
+      fetch_code_ahead<PR>(code, items[2 * (more ? nx : item)], more ? items[2 * nx + 1] : 0u, src, ahead);
+    }
+    auto put = [&](int gi, const uint32_t(&v)[8]) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const u32x4_t av = u32x4_t{v[4 * half], v[4 * half + 1], v[4 * half + 2], v[4 * half + 3]};
+        // The block holding column k - 1 may run past the end of the row
+        // (k not a multiple of 8): zero the activations past it.
+        u32x4_t keep = u32x4_t{~0u, ~0u, ~0u, ~0u};
+        if (a.k & 7u) {
+          const uint32_t col = c0 + 8 * (2 * gi + half), valid = a.k > col ? a.k - col : 0u;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) keep[j] = 2u * j + 1u < valid ? ~0u : 2u * j < valid ? 0xFFFFu : 0u;
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                          __builtin_bit_cast(bf16x8_t, xf[2 * gi + half][h] & keep),
+                                                          acc[h], 0, 0, 0);
+      }
+    };
+    auto run_win = [&](auto &win) {
+      decode_groups<false, NG>([&] { return bf16_step_win(win, lut_lds, a.r2s_lo, a.r2s_hi); }, m, put);
+    };
+    if (wn == 2) {
+      Win<2> win{{cur[0], cur[1]}};
+      run_win(win);
+    } else if (wn == 3) {
+      Win<3> win{{cur[0], cur[1], cur[2]}};
+      run_win(win);
+    } else if (wn == 4) {
+      Win<4> win{{cur[0], cur[1], cur[2], cur[3]}};
+      run_win(win);
+    } else {
+      Lane st{region + 4 * src, lut_lds, 0u, a.r2s_lo, a.r2s_hi};
+      decode_groups<false, NG>([&] { return bf16_step(st); }, m, put);
+    }
+    if (sp + 1 == a.n_spans) {
+      // The row group is done: partials to this wave's slot [h][i][lane],
+      // one barrier, sums over the waves in wave order.
+      const uint32_t buf = parts + parity * W * kPart;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(lds_f32 *)(size_t)(buf + wave * kPart + ((h * 4 + i) * 64 + lane) * 4) = acc[h][i];
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      for (uint32_t e = threadIdx.x; e < (uint32_t)NH * 256; e += blockDim.x) {
+        const uint32_t h = e >> 8, i = (e >> 6) & 3u, l = e & 63u;
+        const uint32_t tok = h * 16 + (l & 15u), row = rg * 16 + (l >> 4) * 4 + i;
+        if (tok < a.batch && row < a.n) {
+          float sum = 0.f;
+          for (uint32_t w = 0; w < W; ++w) sum += *(const lds_f32 *)(size_t)(buf + w * kPart + e * 4);
+          y[(uint64_t)tok * a.ldy + row] = sum;
+        }
+      }
+      parity ^= 1u;
+      sp = 0;
+      rg += grid;
+    } else {
+      ++sp;
+    }
+  }
 }
 
 // Thread t decodes slice t % n_sl of row ids[t / n_sl] (n_sl = ceil(k / C)):
@@ -1263,6 +1439,56 @@ void launch_group_c(const Geom *g, const nwc_matvec_desc *d, int count, hipStrea
   }
 }
 
+// Matrix-core small batch: BF16 blobs of 16 rows per work item and 16 or 32
+// columns per lane; up to 32 activation rows per launch.  A persistent grid of
+// workgroups of the blob's W waves, as many as fit (up to 25 waves per CU),
+// each workgroup one row group at a time.
+constexpr int64_t kMfmaMinBatch = 5;  // fewer rows: the VALU batch kernel
+bool mfma_eligible(const nwc_header_t &h) {
+  return h.elem == NWC_BF16 && h.rows_per_wave == 16 && (h.cols_per_lane == 16 || h.cols_per_lane == 32);
+}
+
+template <int NG, int NH>
+void launch_mfma(const Geom &g, hipStream_t s, const void *d_x, int64_t ldx, int64_t batch, float *d_y, int64_t ldy) {
+  const void *kernel = (const void *)matvec_mfma_kernel<NG, NH>;
+  // Items of at most 4 code rows decode from registers; an LDS code region
+  // per wave only when some item is longer.
+  const uint32_t region_words = g.region_words > (4 + NWC_GUARD_ROWS) * 64 ? g.region_words : 0u;
+  const size_t lds = (size_t)g.W * (region_words * 4 + 2 * NH * kMfmaPartBytes);
+  const Residency res = resident_per_cu(kernel, g.W * 64, lds);
+  uint32_t grid = g.n_rowgroups;
+  if (res.per_cu > 0) grid = std::min<uint32_t>(grid, (uint32_t)res.per_cu * res.cus);
+  MfmaArgs a;
+  a.mant = g.blob + g.off_mant;
+  a.n = (uint32_t)g.n;
+  a.k = (uint32_t)g.k;
+  a.ldx = (uint32_t)ldx;
+  a.ldy = (uint32_t)ldy;
+  a.batch = (uint32_t)batch;
+  a.region_words = region_words;
+  a.r2s_lo = g.r2s_lo;
+  a.r2s_hi = g.r2s_hi;
+  a.n_spans = g.n_spans;
+  hipLaunchKernelGGL((matvec_mfma_kernel<NG, NH>), dim3(grid), dim3(g.W * 64), lds, s, item_table(g),
+                     g.blob + g.off_code, g.blob + g.off_lut, (const uint16_t *)d_x, g.n_rowgroups, g.W, a, d_y);
+}
+
+void launch_mfma_c(const Geom &g, hipStream_t s, const uint16_t *x, int64_t ldx, int64_t batch, float *y,
+                   int64_t ldy) {
+  for (int64_t b = 0; b < batch; b += 32) {
+    const int64_t nb = std::min<int64_t>(32, batch - b);
+    const uint16_t *xb = x + b * ldx;
+    float *yb = y + b * ldy;
+    if (g.C == 16) {
+      if (nb > 16) launch_mfma<1, 2>(g, s, xb, ldx, nb, yb, ldy);
+      else launch_mfma<1, 1>(g, s, xb, ldx, nb, yb, ldy);
+    } else {
+      if (nb > 16) launch_mfma<2, 2>(g, s, xb, ldx, nb, yb, ldy);
+      else launch_mfma<2, 1>(g, s, xb, ldx, nb, yb, ldy);
+    }
+  }
+}
+
 // B = 2 or 4 activation rows of a BF16 blob with one span per row and 16 or
 // 32 columns per lane (wider items would not keep B rows of activations in
 // registers).
@@ -1478,6 +1704,10 @@ int nwc_matvec_batch(const void *header, const void *d_blob, const void *d_x, in
   if (!d_blob || !d_x || !d_y || !aligned(d_blob, 16) || !aligned(d_x, 16) || !aligned(d_y, 4)) return NWC_ERR_ARG;
   if (fp8 != (d_scale != nullptr) || (d_scale && !aligned(d_scale, 4))) return NWC_ERR_ARG;
   const uint16_t *x = (const uint16_t *)d_x;
+  if (mfma_eligible(h) && batch >= kMfmaMinBatch && ldx < ((int64_t)1 << 25)) {  // matrix cores, 32 rows per decode
+    launch_mfma_c(make_geom(h, d_blob), (hipStream_t)stream, x, ldx, batch, d_y, ldy);
+    return launched();
+  }
   if (fp8 || h.n_spans > 1 || h.cols_per_lane > 32) {  // one activation row at a time
     for (int64_t b = 0; b < batch; ++b)
       if ((st = nwc_matvec(header, d_blob, x + b * ldx, d_scale, d_y + b * ldy, d_ws, ws_bytes, stream)) != NWC_OK)

@@ -206,11 +206,19 @@ int nwc_matvec_group(const nwc_matvec_desc *mats, int count, void *stream);
  *            elements; ldx >= k and a multiple of 8 (16-byte aligned rows).
  *   d_y      device, batch rows of n fp32, row b at d_y + b*ldy; ldy >= n.
  *   d_scale, d_ws, ws_bytes: as nwc_matvec (rows share the workspace in turn).
- * BF16 blobs with one span per row and at most 32 columns per lane decode
- * every weight once per group of up to four rows; other blobs run one row
- * at a time.  Each row is
- * summed in the same order as nwc_matvec, so row b equals nwc_matvec on x_b
- * bit for bit.  batch == 0 does nothing. */
+ * BF16 blobs encoded with 16 rows per wave and 16 or 32 columns per lane
+ * (nwc_encode with rows_per_wave = 16), for 5 rows or more and ldx < 2^25:
+ * the matrix-core path (the pages' planned tensor-core accumulation, "Status
+ * and limitations"): every weight is decoded once per 32 activation rows and
+ * the products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; each
+ * output is within the matvec tolerance of the exact sum (the summation
+ * order differs from nwc_matvec but is fixed: repeated calls give the same
+ * bits), activations past column k are never used, and the workspace is not
+ * used.
+ * Other BF16 blobs with one span per row and at most 32 columns per lane
+ * decode every weight once per group of up to four rows, each row summed in
+ * the same order as nwc_matvec, so row b equals nwc_matvec on x_b bit for
+ * bit; other blobs run one row at a time.  batch == 0 does nothing. */
 int nwc_matvec_batch(const void *header, const void *d_blob, const void *d_x, int64_t ldx, int64_t batch,
                      const float *d_scale, float *d_y, int64_t ldy, void *d_ws, int64_t ws_bytes, void *stream);
 

@@ -547,3 +547,34 @@ def test_blob_file_round_trip_runs_every_kernel(tmp_path):
     x8 = S.activation_bf16(175, 2560)
     y_ref, A = O.matvec_fp8_ref(q, arrays["q_scale"], x8)
     check_tol(run_matvec(d8, x8, scale=arrays["q_scale"]), y_ref, A, "loaded fp8 blob")
+
+
+# ----------------------------------------------------------------- matrix-core small batches
+@pytest.mark.parametrize("cols", [16, 32])
+@pytest.mark.parametrize("batch", [5, 8, 16, 17, 32, 40])
+def test_matvec_batch_matrix_cores(cols, batch):
+    """Blobs of 16 rows per wave take the matrix-core path for 5 or more activation rows: every output of
+    every row within the matvec bound of the oracle's float64 sum; the activations' padding past column k (NaN)
+    is never used; nothing written past a row's outputs."""
+    from oracle import fast as F
+    cases = [("ragged with rare values", S.inject_rare(S.student_t_bf16(91, (1000, 3001)), 92)),
+             ("q shape, rows over three spans", S.normal_bf16(93, (4096, 2560), float(np.float32(C.sigma_for(2560)))))]
+    for what, w in cases:
+        n, k = w.shape
+        print(f"case mfma batch={batch} cols={cols} {what} {n}x{k}", flush=True)
+        dm = nwc.DeviceMatrix(nwc.encode(w, cols_per_lane=cols, rows_per_wave=16), DEV)
+        assert dm.info["rows_per_wave"] == 16 and dm.info["cols_per_lane"] == cols
+        ldx = (k + 7) // 8 * 8 + 16
+        ldy = n + 5
+        xs = [S.activation_bf16(1000 * batch + b, k) for b in range(batch)]
+        xh = np.full((batch, ldx), 0x7FC0, dtype=np.uint16)  # NaN past column k: must not be read
+        for b in range(batch):
+            xh[b, :k] = xs[b]
+        y = torch.full((batch, ldy), float("nan"), dtype=torch.float32, device=DEV)
+        dm.matvec_batch(dev16(xh), y)
+        torch.cuda.synchronize()
+        yh = y.cpu().numpy()
+        assert np.isnan(yh[:, n:]).all(), "wrote past a row's outputs"
+        for b in range(batch):
+            y_ref, A = F.matvec_bf16(w, xs[b])
+            check_tol(yh[b, :n].astype(np.float64), y_ref, A, f"{what}: row {b}")

@@ -465,13 +465,14 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
     fp8 = {}
     for tag, (fn_, fk, seeds) in {"single_1024": (1024, 1024, [C.SINGLE["w_seed"]]),
                                    "gate_9728x2560": (9728, 2560, list(range(600000, 600012)))}.items():
-        qs = []
+        qs, ws16 = [], []
         for sd in seeds:
             if fn_ == 1024:
                 wf = S.normal_bf16(sd, (fn_, fk), C.SINGLE["sigma"])
             else:
                 wf = S.blocked_normal_bf16(sd, (fn_, fk), np.float32(C.sigma_for(fk)))
             qs.append(S.fp8_quantize(wf))
+            ws16.append(wf)
         xf = torch.from_numpy(S.activation_bf16(C.SINGLE["x_seed"], fk).view(np.int16)).to(dev)
         yf = torch.empty(fn_, dtype=torch.float32, device=dev)
         fp8[tag] = {}
@@ -487,6 +488,16 @@ def bench_tied_embedding(args, torch, nwc, S, C, dev):
                                "bits_per_weight_blob": round(dms[0].nbytes * 8 / (fn_ * fk), 4),
                                "rotation": len(dms)}
             del dms
+        # The compressed BF16 matvec of the same weights, timed the same way: what fp8 is compared with.
+        dms = [nwc.DeviceMatrix(nwc.encode(wf), dev) for wf in ws16]
+        reps = max(1, 32 // len(dms))
+        msb = per_call_ms(lambda: [d.matvec(xf, yf) for d in dms], reps) / len(dms)
+        ba = dms[0].info["coded_bits"] / 8.0 + 2 * fk + 4 * fn_
+        fp8[tag]["bf16_same_weights"] = {"us": round(msb * 1e3, 3),
+                                         "compressed_GBps": round(ba / (msb * 1e-3) / 1e9, 1),
+                                         "bits_per_weight_coded": round(dms[0].info["coded_bits"] / (fn_ * fk), 4),
+                                         "rotation": len(dms)}
+        del dms, ws16
     out_j = {"metric": "tied embedding 151936x2560: lm_head GEMV, 4096-id gather, dequant; fp8 e4m3 variant",
              "value": round(algo / (ms_mv * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
              "warmup": args.warmup, "ms_per_step": round(ms_mv, 4), "higher_is_better": True, "scaling": "weak",
@@ -711,6 +722,11 @@ def summarize_workload(run_json, cmd):
                 f"| dequantize the whole matrix | {d['dequant_full']['us']} | {d['dequant_full']['GBps_written']} GB/s written |\n")
         for k, byc in fp8.items():
             for cname, v in byc.items():
+                if cname == "bf16_same_weights":
+                    body += (f"| BF16 compressed matvec {k}, the same weights before fp8 quantization (rotation over "
+                             f"{v['rotation']}) | {v['us']} | {v['compressed_GBps']} GB/s, "
+                             f"{v['bits_per_weight_coded']} coded bits/weight |\n")
+                    continue
                 body += (f"| fp8 matvec {k}, {cname} coder (rotation over {v['rotation']}) | {v['us']} | "
                          f"{v['compressed_GBps']} GB/s, {v['bits_per_weight_coded']} coded bits/weight, "
                          f"{v['bits_per_weight_blob']} blob bits/weight |\n")

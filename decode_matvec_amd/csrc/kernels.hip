@@ -43,7 +43,8 @@
 
 static_assert(offsetof(nwc_header_t, n) == 16 && offsetof(nwc_header_t, k) == 24 &&
                   offsetof(nwc_header_t, rows_per_wave) == 36 && offsetof(nwc_header_t, n_rowgroups) == 48 &&
-                  offsetof(nwc_header_t, max_rows) == 56 && offsetof(nwc_header_t, off_mant) == 88 &&
+                  offsetof(nwc_header_t, max_rows) == 56 && offsetof(nwc_header_t, escape_r) == 60 &&
+                  offsetof(nwc_header_t, off_mant) == 88 &&
                   offsetof(nwc_header_t, off_code) == 96 && offsetof(nwc_header_t, rank_to_sym) == 128,
               "header word offsets read by the group kernel");
 
@@ -62,6 +63,7 @@ struct Geom {
   int64_t n, k;
   uint32_t C, R, S, log2S, W, n_spans, n_rowgroups, n_items, region_words;
   uint32_t r2s_lo, r2s_hi;  // rank_to_sym[0..7], one byte each
+  uint32_t huff;            // fp8 blob of the Huffman coder
   uint64_t off_lut, off_items, off_mant, off_code;
 };
 
@@ -440,6 +442,38 @@ __device__ __forceinline__ float slice_dot_fp8_codes(Step step, const X16 (&xv)[
   return a0 + a1;
 }
 
+// Two fp8 codes of a Huffman-coded stream per window shift: no code escapes
+// the 12-bit peek, so the second code's peek is the first two words shifted by
+// the first code's length (one v_alignbit), and the window shifts once by both
+// lengths (at most 24 bits).  Per pair of weights: 2 table reads and 8 + WN
+// other instructions, against 2 x (4 + WN) for two single steps with their
+// escape tests.  Returns the two values as a BF16 pair.
+template <int WN>
+__device__ __forceinline__ uint32_t fp8_pair_win(Win<WN> &s, uint32_t lut) {
+  const uint32_t ea = lds_load(lut + (s.w[0] & 0x3FFCu));
+  const uint32_t la = ea >> 24;
+  const uint32_t eb = lds_load(lut + (__builtin_amdgcn_alignbit(s.w[1], s.w[0], la) & 0x3FFCu));
+  win_shift(s, la + (eb >> 24));
+  return __builtin_amdgcn_perm(eb, ea, kSelPair);
+}
+
+template <int NG, int WN>
+__device__ __forceinline__ float slice_dot_fp8_pairs_win(Win<WN> &s, uint32_t lut, const X16 (&xv)[NG]) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t p = fp8_pair_win(s, lut);
+      if (j & 1)
+        a1 = dot2(p, xv[gi].v[j], a1);
+      else
+        a0 = dot2(p, xv[gi].v[j], a0);
+    }
+  }
+  return a0 + a1;
+}
+
 // The lane's stream in the wave's LDS region.
 template <int NG>
 __device__ __forceinline__ float slice_dot_fp8(Lane &st, const X16 (&xv)[NG]) {
@@ -479,6 +513,7 @@ struct MvArgs {
   const uint8_t *mant;  // mantissa plane
   uint32_t n, R, n_spans, region_words, r2s_lo, r2s_hi, groups_cap;
   uint32_t ldx, ldy;  // elements between the activation rows / output rows of a batch
+  uint32_t huff;      // fp8 blob of the Huffman coder: no escapes
 };
 
 // y[row] (times the fp8 row scale) with one span per row, else the span's
@@ -568,7 +603,7 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
   // where the compiler would put the first use (after the activation loads,
   // one memory round trip later).
   asm volatile("" ::"s"(off0), "s"(rows0));
-  if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
+  if (FP8 && !a.huff) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   const uint32_t step_rg = SPLIT ? grid / a.n_spans : grid, step_sp = grid - step_rg * a.n_spans;
@@ -610,7 +645,8 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
     float v[B];
     auto run_win = [&](auto &win) {
       if constexpr (FP8)
-        v[0] = slice_dot_fp8_win<NG>(win, lds_addr(s_lut), xv[0]);
+        v[0] = a.huff ? slice_dot_fp8_pairs_win<NG>(win, lds_addr(s_lut), xv[0])
+                      : slice_dot_fp8_win<NG>(win, lds_addr(s_lut), xv[0]);
       else
         slice_dot_bf16_win<NG, B>(win, lds_addr(s_lut), a.r2s_lo, a.r2s_hi, m, xv, v);
     };
@@ -755,10 +791,11 @@ __global__ __launch_bounds__(1024) void matvec_group_kernel(uint32_t head, uint3
   const uint32_t it = (wg - beg) * W + wave;
   const uint32_t off0 = items[2 * it], rows0 = items[2 * it + 1];
   // Header fields as 32-bit words (nwc_header_t: n at word 4, k at 6, R at 9,
-  // row groups at 12, max_rows at 14, off_mant at 22-23, off_code at 24-25,
-  // rank_to_sym at 32); n and k are below 2^31.
+  // row groups at 12, max_rows at 14, escape_r at 15, off_mant at 22-23,
+  // off_code at 24-25, rank_to_sym at 32); n and k are below 2^31.
   const uint32_t *hw = (const uint32_t *)blob;
   const uint32_t n = hw[4], k = hw[6], R = hw[9], n_groups = hw[12], max_rows = hw[14];
+  const uint32_t huff = FP8 ? hw[15] == 0 : 0u;
   const uint32_t om_lo = hw[22], om_hi = hw[23], oc_lo = hw[24], oc_hi = hw[25];
   const uint32_t r2s_lo = hw[32], r2s_hi = hw[33];
   const uint64_t off_mant = ((uint64_t)om_hi << 32) | om_lo, off_code = ((uint64_t)oc_hi << 32) | oc_lo;
@@ -774,6 +811,7 @@ __global__ __launch_bounds__(1024) void matvec_group_kernel(uint32_t head, uint3
   a.groups_cap = (n_groups + grid - 1) / grid;
   a.ldx = 0;
   a.ldy = 0;
+  a.huff = huff;
   matvec_body<FP8, NG, false, 1>(items, blob + off_code, blob + NWC_HEADER_BYTES, x, n_groups, W, grid, wg - beg, k,
                                  log2S, a, tail.scale[m], tail.y[m], nullptr, s_lut, s_dyn, off0, rows0);
 }
@@ -1222,6 +1260,7 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
   g.region_words = (h.max_rows + NWC_GUARD_ROWS) * 64;
   g.r2s_lo = h.rank_to_sym[0] | (h.rank_to_sym[1] << 8) | (h.rank_to_sym[2] << 16) | ((uint32_t)h.rank_to_sym[3] << 24);
   g.r2s_hi = h.rank_to_sym[4] | (h.rank_to_sym[5] << 8) | (h.rank_to_sym[6] << 16) | ((uint32_t)h.rank_to_sym[7] << 24);
+  g.huff = h.elem == NWC_FP8_E4M3 && h.escape_r == 0;
   g.off_lut = h.off_lut;
   g.off_items = h.off_items;
   g.off_mant = h.off_mant;
@@ -1342,6 +1381,7 @@ void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d
   a.r2s_lo = g.r2s_lo;
   a.r2s_hi = g.r2s_hi;
   a.groups_cap = L.groups_cap;
+  a.huff = g.huff;
   hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT, B>), dim3(L.grid), dim3(g.W * 64), L.lds, s, item_table(g),
                      g.blob + g.off_code, g.blob + g.off_lut, (const uint16_t *)d_x, g.n_rowgroups * g.n_spans, g.W,
                      L.grid, (uint32_t)g.k, g.log2S, a, d_scale, d_y, partial);

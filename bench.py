@@ -111,41 +111,46 @@ def time_region(torch, fn, steps, warmup):
 
 
 def cpu_baseline(S, C):
-    """The oracle (decode + float64 matvec) on host cores, on a bounded sample of
-    the layer set: layer 0's q, k, v, o and gate matrices (51 M weights)."""
-    import oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    sample = [s for s in C.QWEN3_4B if s[0] in ("q", "k", "v", "o", "gate")]
+    """The oracle on host cores, on a bounded sample of the layer set: the plain C
+    oracle (oracle/nwc_oracle.c) decodes each of layer 0's seven matrices from its
+    row streams and computes the float64 matvec from the decoded weights, in row
+    blocks on as many threads as the host gives this process (at most 16)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import fast as OF
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
     work, gbytes, weights = [], 0.0, 0
-    for name, n, k in sample:
-        idx = [s[0] for s in C.QWEN3_4B].index(name)
+    for idx, (name, n, k) in enumerate(C.QWEN3_4B):
         ws, xs = C.qwen3_seed(0, idx)
-        w = S.normal_bf16(ws, (n, k), C.sigma_for(k))  # host generator: same shapes and distribution
-        enc = O.encode_bf16(w)
+        w = S.blocked_normal_bf16(ws, (n, k), np.float32(C.sigma_for(k)))  # the benchmarked weights
+        r2s, s2r = OF.rank_table(OF.bf16_histogram(w, threads))
+        blocks, bits = [], 0
+        for r0, r1 in OF._blocks(n, k):
+            stream, start, b = OF.encode_rows_bf16(w[r0:r1], s2r)
+            blocks.append((r0, r1, stream, start, (w[r0:r1] & 0xFF).astype(np.uint8)))
+            bits += b
         del w
-        work.append((enc, S.activation_bf16(xs, k)))
-        gbytes += (enc["coded_bits"] / 8.0 + 2 * k + 4 * n) / 1e9
+        work.append((n, k, r2s, blocks, S.activation_bf16(xs, k)))
+        gbytes += ((bits + 8 * n * k) / 8.0 + 2 * k + 4 * n) / 1e9
         weights += n * k
-    limit = threadpool_limits(1) if threadpool_limits else None
-    # The sample is decoded and multiplied repeatedly until about 10 s of CPU work have passed.
-    passes = 0
-    t0 = time.perf_counter()
-    while passes == 0 or time.perf_counter() - t0 < 10.0:
-        for enc, x in work:
-            y, A = O.matvec_bf16_ref(O.decode_bf16(enc), x)
-        passes += 1
-    dt = time.perf_counter() - t0
-    if limit is not None and hasattr(limit, "unregister"):
-        limit.unregister()
-    return {"value": round(gbytes * passes / dt, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)),
-            "sample": f"oracle decode + float64 matvec of layer 0's q, k, v, o, gate ({weights / 1e6:.1f} M weights, "
-                      f"host PCG64 draws of the same distributions), single thread (BLAS limited to 1), "
-                      f"{passes} passes, {dt:.1f} s"}
 
+    def one(job):
+        k, r2s, (r0, r1, stream, start, mant), x = job
+        return OF.matvec_bf16(OF.decode_rows_bf16(stream, start, r1 - r0, k, r2s, mant), x, threads=1)
+
+    jobs = [(k, r2s, b, x) for n, k, r2s, blocks, x in work for b in blocks]
+    # The sample is decoded and multiplied repeatedly until about 10 s have passed.
+    passes = 0
+    with ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        while passes == 0 or time.perf_counter() - t0 < 10.0:
+            list(ex.map(one, jobs))
+            passes += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(gbytes * passes / dt, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "host_cpus_usable": len(os.sched_getaffinity(0)),
+            "sample": f"C oracle decode + float64 matvec of layer 0's 7 matrices ({weights / 1e6:.1f} M weights, "
+                      f"the benchmarked weights), {len(jobs)} row blocks on {threads} threads, {passes} passes, "
+                      f"{dt:.1f} s"}
 
 def build_qwen25_step(torch, nwc, S, C, dev, layers, with_bf16, with_fused=False):
     """Qwen2.5-7B-shaped decode step: `layers` layers of 7 projections plus the

@@ -64,6 +64,7 @@ struct Geom {
   uint32_t C, R, S, log2S, W, n_spans, n_rowgroups, n_items, region_words;
   uint32_t r2s_lo, r2s_hi;  // rank_to_sym[0..7], one byte each
   uint32_t huff;            // fp8 blob of the Huffman coder
+  uint32_t code_words4;     // code plane bytes (a buffer range; the format keeps offsets below 2^32)
   uint64_t off_lut, off_items, off_mant, off_code;
 };
 
@@ -1197,21 +1198,27 @@ __global__ __launch_bounds__(1024) void matvec_mfma_kernel(const uint32_t *__res
   }
 }
 
-// Thread t decodes slice t % n_sl of row ids[t / n_sl] (n_sl = ceil(k / C)):
-// it copies that slice's stream from its item into its own LDS column, then
-// decodes it like the matvec does.  Ids outside [0, n) give a zero row.
+// Thread t decodes slice t % n_sl of row ids[t / n_sl] (n_sl = ceil(k / C)).
+// Ids outside [0, n) give a zero row.  Everything a thread needs is requested
+// as soon as its address is known: the id, then its item-table entry, then at
+// once its code words (a window's worth, zero past the item's rows: bounds-
+// checked buffer loads over the code plane) and its mantissa chunks; the
+// decode table is copied meanwhile.  The wave then decodes from a register
+// window sized to its longest item, as the matvec does.  A wave with a longer
+// item (wider than the window) copies each lane's stream to its LDS column
+// and decodes from there.
 template <bool FP8, int NG>
 __global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__restrict__ items,
                                                       const int64_t *__restrict__ ids, int64_t n_ids,
                                                       uint32_t n_sl, uint8_t *__restrict__ out) {
+  constexpr uint32_t kWinMax = FP8 ? 6u : 4u;
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t waves = blockDim.x >> 6;
-  dma_lut(g, lds_addr(s_lut), wave, waves, lane);
-  if (FP8) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
-  const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
+  const uint32_t lut = lds_addr(s_lut);
+  dma_lut(g, lut, wave, waves, lane);
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tok = t / n_sl;
   const uint32_t q = (uint32_t)(t - tok * n_sl);
@@ -1224,23 +1231,68 @@ __global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__
   const uint32_t span = wq / g.W, wv = wq - span * g.W;
   const uint32_t item = (rg * g.n_spans + span) * g.W + wv, L = r * g.S + s;
   const uint32_t off = items[2 * item], rows = items[2 * item + 1];
-  const uint32_t *src = (const uint32_t *)(g.blob + g.off_code + off) + L;
-  for (uint32_t i = 0; i < rows; ++i) lds_store(region + i * 256 + 4 * lane, src[i * 64]);
-  lds_store(region + rows * 256 + 4 * lane, 0u);
-  lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
-  staged_barrier();
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(g.blob + g.off_code), (short)0, (int)g.code_words4, kBufWord3);
+  uint32_t w[kWinMax];
+#pragma unroll
+  for (uint32_t j = 0; j < kWinMax; ++j)
+    w[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, j < rows ? off + j * 256 + 4 * L : 0xFFFFFFF0u, 0, 0);
+  uint4 m[NG];
+  if (!FP8) {
+    const uint4 *mp = mant_base(g, item, L);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) m[gi] = mp[gi * 64];
+  }
+  if (FP8) build_fp8_escapes(lut + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
+  wait_vm0();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
   const int64_t esz = FP8 ? 1 : 2;
   const int64_t c0 = (int64_t)q * g.C;
   uint8_t *dst = out + (tok * g.k + c0) * esz;
   const bool vec = (g.k * esz) % 16 == 0;
-  if (valid) {
-    Lane st{region + 4 * lane, lds_addr(s_lut), 0u, g.r2s_lo, g.r2s_hi};
-    slice_decode<FP8, NG>(st, FP8 ? nullptr : mant_base(g, item, L), [&](int gi, const uint32_t(&v)[8]) {
-      put_group<FP8>(dst + 16 * gi * esz, v, g.k - c0 - 16 * gi, vec);
-    });
-  } else if (live) {
-    const uint32_t zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int gi = 0; gi < NG; ++gi) put_group<FP8>(dst + 16 * gi * esz, zero, g.k - c0 - 16 * gi, vec);
+  const int64_t left = live ? g.k - c0 : 0;
+  auto put = [&](int gi, const uint32_t(&v)[8]) {
+    uint32_t z[8];  // an id outside [0, n): zeros (its lane decoded row 0)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = valid ? v[i] : 0u;
+    put_group<FP8>(dst + 16 * gi * esz, z, left - 16 * gi, vec);
+  };
+  // Window size: the longest item among the wave's live lanes.
+  const uint32_t rl = valid ? rows : 0u;
+  const uint32_t wn = __any(rl > kWinMax) ? 0u : __any(rl > 4) ? (__any(rl > 5) ? 6u : 5u)
+                      : __any(rl > 3) ? 4u : __any(rl > 2) ? 3u : 2u;
+  auto run_win = [&](auto &win) {
+    if constexpr (FP8)
+      decode_groups<true, NG>([&] { return fp8_step_win(win, lut); }, m, put);
+    else
+      decode_groups<false, NG>([&] { return bf16_step_win(win, lut, g.r2s_lo, g.r2s_hi); }, m, put);
+  };
+  if (wn == 2) {
+    Win<2> win{{w[0], w[1]}};
+    run_win(win);
+  } else if (wn == 3) {
+    Win<3> win{{w[0], w[1], w[2]}};
+    run_win(win);
+  } else if (wn == 4) {
+    Win<4> win{{w[0], w[1], w[2], w[3]}};
+    run_win(win);
+  } else if (FP8 && wn == 5) {
+    Win<5> win{{w[0], w[1], w[2], w[3], w[kWinMax > 4 ? 4 : 0]}};
+    run_win(win);
+  } else if (FP8 && wn == 6) {
+    Win<6> win{{w[0], w[1], w[2], w[3], w[kWinMax > 4 ? 4 : 0], w[kWinMax > 5 ? 5 : 0]}};
+    run_win(win);
+  } else {
+    // Some lane's item is longer than the window: every lane's stream to its
+    // LDS column (a lane reads only its own column: no barrier).
+    const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
+    const uint32_t *src = (const uint32_t *)(g.blob + g.off_code + off) + L;
+    for (uint32_t i = 0; i < rows; ++i) lds_store(region + i * 256 + 4 * lane, src[i * 64]);
+    lds_store(region + rows * 256 + 4 * lane, 0u);
+    lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
+    Lane st{region + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
+    slice_decode<FP8, NG>(st, FP8 ? nullptr : mant_base(g, item, L), put);
   }
 }
 
@@ -1261,6 +1313,7 @@ Geom make_geom(const nwc_header_t &h, const void *d_blob) {
   g.r2s_lo = h.rank_to_sym[0] | (h.rank_to_sym[1] << 8) | (h.rank_to_sym[2] << 16) | ((uint32_t)h.rank_to_sym[3] << 24);
   g.r2s_hi = h.rank_to_sym[4] | (h.rank_to_sym[5] << 8) | (h.rank_to_sym[6] << 16) | ((uint32_t)h.rank_to_sym[7] << 24);
   g.huff = h.elem == NWC_FP8_E4M3 && h.escape_r == 0;
+  g.code_words4 = (uint32_t)std::min<uint64_t>(h.code_bytes, 0xFFFFFFF0u);
   g.off_lut = h.off_lut;
   g.off_items = h.off_items;
   g.off_mant = h.off_mant;

@@ -1198,20 +1198,24 @@ __global__ __launch_bounds__(1024) void matvec_mfma_kernel(const uint32_t *__res
   }
 }
 
-// Thread t decodes slice t % n_sl of row ids[t / n_sl] (n_sl = ceil(k / C)).
-// Ids outside [0, n) give a zero row.  Everything a thread needs is requested
-// as soon as its address is known: the id, then its item-table entry, then at
-// once its code words (a window's worth, zero past the item's rows: bounds-
-// checked buffer loads over the code plane) and its mantissa chunks; the
-// decode table is copied meanwhile.  The wave then decodes from a register
-// window sized to its longest item, as the matvec does.  A wave with a longer
-// item (wider than the window) copies each lane's stream to its LDS column
-// and decodes from there.
+// A (token, slice) unit u decodes slice u % n_sl of row ids[u / n_sl]
+// (n_sl = ceil(k / C)); ids outside [0, n) give a zero row.  Thread t takes
+// the units t + j * T (T threads in all, j < kGatherUnits), so the whole grid
+// is resident at once.  Everything a unit needs is requested as soon as its
+// address is known: the id, then its item-table entry, then at once its code
+// words (a window's worth, zero past the item's rows: bounds-checked buffer
+// loads over the code plane) and its mantissa chunks, for every unit of the
+// thread before the one wait; the decode table is copied meanwhile.  Each
+// unit is then decoded from a register window sized to the longest item among
+// the wave's lanes, as the matvec does; a wave with an item longer than the
+// window copies each lane's stream to its LDS column and decodes from there.
+constexpr int kGatherUnits = 2;
 template <bool FP8, int NG>
-__global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__restrict__ items,
-                                                      const int64_t *__restrict__ ids, int64_t n_ids,
-                                                      uint32_t n_sl, uint8_t *__restrict__ out) {
+__global__ __launch_bounds__(512) void gather_kernel(Geom g, const uint32_t *__restrict__ items,
+                                                     const int64_t *__restrict__ ids, int64_t n_ids, uint32_t n_sl,
+                                                     uint8_t *__restrict__ out) {
   constexpr uint32_t kWinMax = FP8 ? 6u : 4u;
+  constexpr int U = kGatherUnits;
   __shared__ uint32_t s_lut[NWC_LUT_ENTRIES + (FP8 ? NWC_FP8_ESC_ENTRIES : 0)];
   extern __shared__ uint32_t s_dyn[];
   const uint32_t lane = threadIdx.x & 63u;
@@ -1219,80 +1223,107 @@ __global__ __launch_bounds__(1024) void gather_kernel(Geom g, const uint32_t *__
   const uint32_t waves = blockDim.x >> 6;
   const uint32_t lut = lds_addr(s_lut);
   dma_lut(g, lut, wave, waves, lane);
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t tok = t / n_sl;
-  const uint32_t q = (uint32_t)(t - tok * n_sl);
-  const bool live = tok < n_ids;
-  const int64_t id = live ? ids[tok] : 0;
-  const bool valid = live && id >= 0 && id < g.n;
-  const int64_t row = valid ? id : 0;
-  const uint32_t rg = (uint32_t)(row / g.R), r = (uint32_t)(row - (int64_t)rg * g.R);
-  const uint32_t wq = q >> g.log2S, s = q & (g.S - 1u);
-  const uint32_t span = wq / g.W, wv = wq - span * g.W;
-  const uint32_t item = (rg * g.n_spans + span) * g.W + wv, L = r * g.S + s;
-  const uint32_t off = items[2 * item], rows = items[2 * item + 1];
+  const int64_t T = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const __amdgpu_buffer_rsrc_t cr =
       __builtin_amdgcn_make_buffer_rsrc((void *)(g.blob + g.off_code), (short)0, (int)g.code_words4, kBufWord3);
-  uint32_t w[kWinMax];
+  int64_t tok[U];
+  uint32_t q[U], item[U], L[U], off[U], rows[U];
+  bool live[U], valid[U];
 #pragma unroll
-  for (uint32_t j = 0; j < kWinMax; ++j)
-    w[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, j < rows ? off + j * 256 + 4 * L : 0xFFFFFFF0u, 0, 0);
-  uint4 m[NG];
-  if (!FP8) {
-    const uint4 *mp = mant_base(g, item, L);
+  for (int u = 0; u < U; ++u) {
+    const int64_t t = t0 + u * T;
+    tok[u] = t / n_sl;
+    q[u] = (uint32_t)(t - tok[u] * n_sl);
+    live[u] = tok[u] < n_ids;
+  }
+  int64_t id[U];
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) m[gi] = mp[gi * 64];
+  for (int u = 0; u < U; ++u) id[u] = live[u] ? ids[tok[u]] : 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    valid[u] = live[u] && id[u] >= 0 && id[u] < g.n;
+    const int64_t row = valid[u] ? id[u] : 0;
+    const uint32_t rg = (uint32_t)(row / g.R), r = (uint32_t)(row - (int64_t)rg * g.R);
+    const uint32_t wq = q[u] >> g.log2S, sl = q[u] & (g.S - 1u);
+    const uint32_t span = wq / g.W, wv = wq - span * g.W;
+    item[u] = (rg * g.n_spans + span) * g.W + wv;
+    L[u] = r * g.S + sl;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    off[u] = items[2 * item[u]];
+    rows[u] = items[2 * item[u] + 1];
+  }
+  uint32_t w[U][kWinMax];
+  uint4 m[U][NG];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (uint32_t j = 0; j < kWinMax; ++j)
+      w[u][j] = __builtin_amdgcn_raw_buffer_load_b32(cr, j < rows[u] ? off[u] + j * 256 + 4 * L[u] : 0xFFFFFFF0u,
+                                                     0, 0);
+    if (!FP8) {
+      const uint4 *mp = mant_base(g, item[u], L[u]);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) m[u][gi] = mp[gi * 64];
+    }
   }
   if (FP8) build_fp8_escapes(lut + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   wait_vm0();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   const int64_t esz = FP8 ? 1 : 2;
-  const int64_t c0 = (int64_t)q * g.C;
-  uint8_t *dst = out + (tok * g.k + c0) * esz;
   const bool vec = (g.k * esz) % 16 == 0;
-  const int64_t left = live ? g.k - c0 : 0;
-  auto put = [&](int gi, const uint32_t(&v)[8]) {
-    uint32_t z[8];  // an id outside [0, n): zeros (its lane decoded row 0)
+  const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = valid ? v[i] : 0u;
-    put_group<FP8>(dst + 16 * gi * esz, z, left - 16 * gi, vec);
-  };
-  // Window size: the longest item among the wave's live lanes.
-  const uint32_t rl = valid ? rows : 0u;
-  const uint32_t wn = __any(rl > kWinMax) ? 0u : __any(rl > 4) ? (__any(rl > 5) ? 6u : 5u)
-                      : __any(rl > 3) ? 4u : __any(rl > 2) ? 3u : 2u;
-  auto run_win = [&](auto &win) {
-    if constexpr (FP8)
-      decode_groups<true, NG>([&] { return fp8_step_win(win, lut); }, m, put);
-    else
-      decode_groups<false, NG>([&] { return bf16_step_win(win, lut, g.r2s_lo, g.r2s_hi); }, m, put);
-  };
-  if (wn == 2) {
-    Win<2> win{{w[0], w[1]}};
-    run_win(win);
-  } else if (wn == 3) {
-    Win<3> win{{w[0], w[1], w[2]}};
-    run_win(win);
-  } else if (wn == 4) {
-    Win<4> win{{w[0], w[1], w[2], w[3]}};
-    run_win(win);
-  } else if (FP8 && wn == 5) {
-    Win<5> win{{w[0], w[1], w[2], w[3], w[kWinMax > 4 ? 4 : 0]}};
-    run_win(win);
-  } else if (FP8 && wn == 6) {
-    Win<6> win{{w[0], w[1], w[2], w[3], w[kWinMax > 4 ? 4 : 0], w[kWinMax > 5 ? 5 : 0]}};
-    run_win(win);
-  } else {
-    // Some lane's item is longer than the window: every lane's stream to its
-    // LDS column (a lane reads only its own column: no barrier).
-    const uint32_t region = lds_addr(s_dyn) + wave * g.region_words * 4;
-    const uint32_t *src = (const uint32_t *)(g.blob + g.off_code + off) + L;
-    for (uint32_t i = 0; i < rows; ++i) lds_store(region + i * 256 + 4 * lane, src[i * 64]);
-    lds_store(region + rows * 256 + 4 * lane, 0u);
-    lds_store(region + (rows + 1) * 256 + 4 * lane, 0u);
-    Lane st{region + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
-    slice_decode<FP8, NG>(st, FP8 ? nullptr : mant_base(g, item, L), put);
+  for (int u = 0; u < U; ++u) {
+    const int64_t c0 = (int64_t)q[u] * g.C;
+    uint8_t *dst = out + (tok[u] * g.k + c0) * esz;
+    const int64_t left = live[u] ? g.k - c0 : 0;
+    const bool ok = valid[u];
+    auto put = [&](int gi, const uint32_t(&v)[8]) {
+      uint32_t z[8];  // an id outside [0, n): zeros (its lane decoded row 0)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = ok ? v[i] : 0u;
+      put_group<FP8>(dst + 16 * gi * esz, z, left - 16 * gi, vec);
+    };
+    // Window size: the longest item among the wave's live lanes.
+    const uint32_t rl = ok ? rows[u] : 0u;
+    const uint32_t wn = __any(rl > kWinMax) ? 0u : __any(rl > 4) ? (__any(rl > 5) ? 6u : 5u)
+                        : __any(rl > 3) ? 4u : __any(rl > 2) ? 3u : 2u;
+    auto run_win = [&](auto &win) {
+      if constexpr (FP8)
+        decode_groups<true, NG>([&] { return fp8_step_win(win, lut); }, m[u], put);
+      else
+        decode_groups<false, NG>([&] { return bf16_step_win(win, lut, g.r2s_lo, g.r2s_hi); }, m[u], put);
+    };
+    const uint32_t(&ww)[kWinMax] = w[u];
+    if (wn == 2) {
+      Win<2> win{{ww[0], ww[1]}};
+      run_win(win);
+    } else if (wn == 3) {
+      Win<3> win{{ww[0], ww[1], ww[2]}};
+      run_win(win);
+    } else if (wn == 4) {
+      Win<4> win{{ww[0], ww[1], ww[2], ww[3]}};
+      run_win(win);
+    } else if (FP8 && wn == 5) {
+      Win<5> win{{ww[0], ww[1], ww[2], ww[3], ww[kWinMax > 4 ? 4 : 0]}};
+      run_win(win);
+    } else if (FP8 && wn == 6) {
+      Win<6> win{{ww[0], ww[1], ww[2], ww[3], ww[kWinMax > 4 ? 4 : 0], ww[kWinMax > 5 ? 5 : 0]}};
+      run_win(win);
+    } else {
+      // Some lane's item is longer than the window: every lane's stream to its
+      // LDS column (a lane reads and writes only its own column, in order).
+      const uint32_t *src = (const uint32_t *)(g.blob + g.off_code + off[u]) + L[u];
+      for (uint32_t i = 0; i < rows[u]; ++i) lds_store(region + i * 256 + 4 * lane, src[i * 64]);
+      lds_store(region + rows[u] * 256 + 4 * lane, 0u);
+      lds_store(region + (rows[u] + 1) * 256 + 4 * lane, 0u);
+      Lane st{region + 4 * lane, lut, 0u, g.r2s_lo, g.r2s_hi};
+      slice_decode<FP8, NG>(st, FP8 ? nullptr : mant_base(g, item[u], L[u]), put);
+    }
   }
 }
 
@@ -1632,10 +1663,13 @@ void launch_dequant_c(const Geom &g, hipStream_t s, void *d_w, int64_t ld) {
 template <bool FP8, int NG>
 void launch_gather(const Geom &g, hipStream_t s, const int64_t *d_ids, int64_t n_ids, void *d_out) {
   const uint32_t n_sl = (uint32_t)((g.k + g.C - 1) / g.C);
-  const int64_t threads = n_ids * n_sl;
+  const int64_t units = n_ids * n_sl;
+  // Workgroups of 8 waves (or as many as the LDS regions allow), each thread
+  // kGatherUnits units: the grid of a 4096-id gather is resident at once.
   const uint32_t fit = (uint32_t)((NWC_LDS_BUDGET - NWC_LUT_BYTES) / (g.region_words * 4));
-  const uint32_t waves = fit < 1 ? 1 : fit > 16 ? 16 : fit;
+  const uint32_t waves = fit < 1 ? 1 : fit > 8 ? 8 : fit;
   const uint32_t tpb = waves * 64;
+  const int64_t threads = (units + kGatherUnits - 1) / kGatherUnits;
   hipLaunchKernelGGL((gather_kernel<FP8, NG>), dim3((unsigned)((threads + tpb - 1) / tpb)), dim3(tpb),
                      (size_t)waves * g.region_words * 4, s, g, item_table(g), d_ids, n_ids, n_sl, (uint8_t *)d_out);
 }

@@ -21,6 +21,12 @@ SRC = os.path.join(ROOT, "decode_matvec_amd", "csrc", "kernels.hip")
 VMEM = ("global_load", "buffer_load", "global_store", "buffer_store", "global_atomic", "buffer_atomic")
 
 
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    """The library's kernels compiled for gfx950 to AMD assembly, once for this module."""
+    return _assembly(tmp_path_factory.mktemp("isa"))
+
+
 def _assembly(tmp_path):
     out = str(tmp_path / "kernels.s")
     from decode_matvec_amd.build import FLAGS
@@ -123,8 +129,7 @@ def test_dataflow_finds_a_planted_hazard():
     assert hazards(safe) == []
 
 
-def test_every_lds_read_waits_for_the_lds_dma(tmp_path):
-    asm = _assembly(tmp_path)
+def test_every_lds_read_waits_for_the_lds_dma(asm):
     checked = 0
     bad = {}
     for name, body in _kernels(asm):
@@ -135,4 +140,15 @@ def test_every_lds_read_waits_for_the_lds_dma(tmp_path):
         if h:
             bad[name] = h[:3]
     assert checked >= 20, checked          # matvec, group, dequant and gather instances
+    assert not bad, bad
+
+
+def test_gather_code_base_is_not_sign_extended(asm):
+    """Regression: a helper that restated a pointer as wave-uniform widened the signed 32-bit result of
+    readfirstlane into the pointer's high word, so the gather's code-plane buffer base became 0xFFFF_xxxxxxxx
+    whenever bit 31 of the low word was set (a GPU memory fault).  No gather kernel sign-extends a 32-bit
+    value into 64 bits."""
+    gathers = [(name, body) for name, body in _kernels(asm) if "gather_kernel" in name]
+    assert len(gathers) >= 8, len(gathers)
+    bad = [name for name, body in gathers if "s_bfe_i64" in body]
     assert not bad, bad

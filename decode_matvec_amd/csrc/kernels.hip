@@ -281,9 +281,8 @@ __device__ __forceinline__ void dma_lut(const Geom &g, uint32_t lut, uint32_t wa
 
 __device__ __forceinline__ void lds_store(uint32_t byte_addr, uint32_t v) { *(lds_u32 *)(size_t)byte_addr = v; }
 
-__device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// The same waits as builtins, which the compiler's own wait placement takes
-// into account (it does not read inline assembly): vmcnt(0), lgkmcnt(0).
+// Waits as builtins, which the compiler's own wait placement takes into
+// account (it does not read inline assembly): vmcnt(0), lgkmcnt(0).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -310,7 +309,9 @@ __device__ __forceinline__ void fetch_code_ahead(const uint8_t *code, uint32_t o
 
 // Puts a fetched item into the wave's LDS region: the PR register rows (the
 // rows the region holds), then, for an item longer than PR - 2 rows, its other
-// rows straight from memory and the two zero guard rows.
+// rows straight from memory and the two zero guard rows.  col is the item lane
+// whose stream this lane fetched (its column of the region; the lane itself
+// except in the matrix-core kernel); lane moves its share of the copy.
 template <int PR>
 __device__ __forceinline__ void commit_code_ahead(const uint8_t *code, uint32_t off, uint32_t rows,
                                                   uint32_t region_rows, uint32_t region, uint32_t lane,
@@ -324,15 +325,6 @@ __device__ __forceinline__ void commit_code_ahead(const uint8_t *code, uint32_t 
     lds_store(region + (rows + 1) * 256 + 4 * col, 0u);
     wait_vm0();
   }
-}
-
-// Waits for this wave's loads (its LDS copies included), then a bare barrier
-// makes every wave's copies visible.
-__device__ __forceinline__ void staged_barrier() {
-  wait_all_loads();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS writes too (the fp8 escape table)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Activation pairs of 16 columns from column c; columns at or past k are 0.

@@ -565,14 +565,17 @@ __device__ __forceinline__ void stage_lut(const uint8_t *lut, uint32_t *s_lut, u
 // item table and keeps the item-table reads in the loop scalar loads.  s_lut: the static decode table (and
 // fp8 escape table); s_dyn: one code region per wave, then groups_cap slots of
 // W*R row sums (matvec_lds on the host sizes it).
-template <bool FP8, int NG, bool SPLIT, int B>
+template <bool FP8, int NG, bool SPLIT, int B, int LS = -1>
 __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
                                             const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
                                             uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t first, uint32_t k,
-                                            uint32_t log2S, const MvArgs &a, const float *__restrict__ scale,
+                                            uint32_t log2S_arg, const MvArgs &a, const float *__restrict__ scale,
                                             float *__restrict__ y, float *__restrict__ partial, uint32_t *s_lut,
                                             uint32_t *s_dyn, uint32_t off0, uint32_t rows0) {
   constexpr uint32_t C = 16 * NG;
+  // Lanes per row as a constant where the caller knows it (the row sums then
+  // take no branches).
+  const uint32_t log2S = LS >= 0 ? (uint32_t)LS : log2S_arg;
   // Code rows fetched ahead: a BF16 item's rows and its guard rows, typically;
   // an fp8 item (6.75 bits per weight) takes 4 to 6 rows of 16-column slices.
   constexpr int PR = FP8 ? 2 * NG + 4 : 2 * NG + 2;
@@ -582,7 +585,9 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
   // Workgroup b takes groups b, b + grid, b + 2*grid, ...: at any time the
   // workgroups read neighbouring items, so the machine streams the planes in
   // order.
-  const uint32_t n_mine = (n_groups - first + grid - 1) / grid;
+  // A scalar: the division would otherwise leave it, and every test of the
+  // item count, in vector registers.
+  const uint32_t n_mine = __builtin_amdgcn_readfirstlane((n_groups - first + grid - 1) / grid);
   const uint32_t region = lds_addr(s_dyn) + wave * a.region_words * 4;  // LDS byte address
   const uint32_t region_rows = a.region_words >> 6;
   float *red = (float *)(s_dyn + W * a.region_words);  // [group][wave][activation row][R]
@@ -600,26 +605,33 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
   const uint32_t step_rg = SPLIT ? grid / a.n_spans : grid, step_sp = grid - step_rg * a.n_spans;
-  X16 xv[B][NG];
-  load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
   uint32_t ahead[PR];
   fetch_code_ahead<PR>(code, off0, rows0, lane, ahead);
   wait_vm0();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
+  // The activations after the barrier: the first decode does not need them,
+  // and every workgroup of a launch reads the same few KiB at its start.
+  // Measured on MI355X, waiting for them with the decode table made the
+  // Qwen3-4B layer set 3.5 % slower (1.484 vs 1.433 ms per sweep).
+  X16 xv[B][NG];
+  load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
 
+  // The item-table entry of the item whose rows are in flight, read when they
+  // were fetched.
+  uint32_t off_next = off0, rows_next = rows0;
   for (uint32_t i = 0, grp = first; i < n_mine; ++i, grp += grid) {
     const uint32_t item = grp * W + wave;
     // Items of at most kWinMax code rows (BF16: 4, fp8: 6) decode from a
     // register window of that many words (at least two); longer ones from the
     // wave's LDS region.
-    const uint32_t rows = items[2 * item + 1];
+    const uint32_t rows = rows_next, off = off_next;
     const uint32_t wn = rows > kWinMax ? 0u : rows < 2u ? 2u : rows;
     if (SPLIT && grp != first) load_x_slice<NG, B>(x, a.ldx, k, xv, ((sp * W + wave) << log2S) * C + lane_c);
     uint32_t cur[kWinMax];
 #pragma unroll
     for (uint32_t j = 0; j < kWinMax; ++j) cur[j] = ahead[j];
-    if (wn == 0) commit_code_ahead<PR>(code, items[2 * item], rows, region_rows, region, lane, ahead, lane);
+    if (wn == 0) commit_code_ahead<PR>(code, off, rows, region_rows, region, lane, ahead, lane);
     // Mantissas of this item, then the next item's code rows: the decode below
     // needs neither, so both stream in while it runs (the compiler waits for
     // the mantissas at the multiply-adds, which it places after the decode
@@ -633,7 +645,9 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
     {
       const bool more = i + 1 < n_mine;
       const uint32_t nx = more ? item + grid * W : item;
-      fetch_code_ahead<PR>(code, items[2 * nx], more ? items[2 * nx + 1] : 0u, lane, ahead);
+      off_next = items[2 * nx];
+      rows_next = more ? items[2 * nx + 1] : 0u;
+      fetch_code_ahead<PR>(code, off_next, rows_next, lane, ahead);
     }
     float v[B];
     auto run_win = [&](auto &win) {
@@ -699,7 +713,7 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
   }
 }
 
-template <bool FP8, int NG, bool SPLIT, int B>
+template <bool FP8, int NG, bool SPLIT, int B, int LS = -1>
 __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict__ items, const uint8_t *__restrict__ code,
                                                       const uint8_t *__restrict__ lut, const uint16_t *__restrict__ x,
                                                       uint32_t n_groups, uint32_t W, uint32_t grid, uint32_t k,
@@ -710,8 +724,8 @@ __global__ __launch_bounds__(1024) void matvec_kernel(const uint32_t *__restrict
   extern __shared__ uint32_t s_dyn[];
   const uint32_t it = blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t off0 = items[2 * it], rows0 = items[2 * it + 1];
-  matvec_body<FP8, NG, SPLIT, B>(items, code, lut, x, n_groups, W, grid, blockIdx.x, k, log2S, a, scale, y, partial,
-                                 s_lut, s_dyn, off0, rows0);
+  matvec_body<FP8, NG, SPLIT, B, LS>(items, code, lut, x, n_groups, W, grid, blockIdx.x, k, log2S, a, scale, y,
+                                     partial, s_lut, s_dyn, off0, rows0);
 }
 
 // Several matrices of one work-item shape (elem, C, R, W; rows within one
@@ -740,7 +754,7 @@ struct GroupTail {
   float *y[kGroupMax];
 };
 
-template <bool FP8, int NG>
+template <bool FP8, int NG, int LS = -1>
 __global__ __launch_bounds__(1024) void matvec_group_kernel(uint32_t head, uint32_t begins,
                                                             const uint8_t *__restrict__ blob0,
                                                             const uint8_t *__restrict__ blob1,
@@ -805,8 +819,8 @@ __global__ __launch_bounds__(1024) void matvec_group_kernel(uint32_t head, uint3
   a.ldx = 0;
   a.ldy = 0;
   a.huff = huff;
-  matvec_body<FP8, NG, false, 1>(items, blob + off_code, blob + NWC_HEADER_BYTES, x, n_groups, W, grid, wg - beg, k,
-                                 log2S, a, tail.scale[m], tail.y[m], nullptr, s_lut, s_dyn, off0, rows0);
+  matvec_body<FP8, NG, false, 1, LS>(items, blob + off_code, blob + NWC_HEADER_BYTES, x, n_groups, W, grid, wg - beg,
+                                     k, log2S, a, tail.scale[m], tail.y[m], nullptr, s_lut, s_dyn, off0, rows0);
 }
 
 // y[row] = (scale[row] *) sum over column spans of the partials, 16 threads
@@ -1441,10 +1455,10 @@ Launch matvec_launch_shape(const Geom &g, const void *kernel, uint32_t B = 1, si
 
 // B activation rows at once (x rows ldx elements apart, y rows ldy apart);
 // B > 1 only for BF16 blobs whose rows fit one workgroup.
-template <bool FP8, int NG, bool SPLIT, int B = 1>
-void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial,
-                   int64_t ldx = 0, int64_t ldy = 0) {
-  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT, B>, B,
+template <bool FP8, int NG, bool SPLIT, int B, int LS>
+void launch_matvec_ls(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial,
+                      int64_t ldx, int64_t ldy) {
+  const Launch L = matvec_launch_shape(g, (const void *)matvec_kernel<FP8, NG, SPLIT, B, LS>, B,
                                        NWC_LUT_BYTES + (FP8 ? NWC_FP8_ESC_ENTRIES * 4 : 0));
   MvArgs a;
   a.ldx = (uint32_t)ldx;
@@ -1458,12 +1472,26 @@ void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d
   a.r2s_hi = g.r2s_hi;
   a.groups_cap = L.groups_cap;
   a.huff = g.huff;
-  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT, B>), dim3(L.grid), dim3(g.W * 64), L.lds, s, item_table(g),
+  hipLaunchKernelGGL((matvec_kernel<FP8, NG, SPLIT, B, LS>), dim3(L.grid), dim3(g.W * 64), L.lds, s, item_table(g),
                      g.blob + g.off_code, g.blob + g.off_lut, (const uint16_t *)d_x, g.n_rowgroups * g.n_spans, g.W,
                      L.grid, (uint32_t)g.k, g.log2S, a, d_scale, d_y, partial);
   if (g.n_spans > 1)
     hipLaunchKernelGGL((reduce_kernel<FP8>), dim3((unsigned)((g.n * 16 + 255) / 256)), dim3(256), 0, s, partial,
                        g.n_spans, g.n, d_scale, d_y);
+}
+
+// Rows of 32 or 64 lanes (S) take kernels built for that S, whose row sums
+// need no branches: for one-span, batch-1 launches of 16- and 32-column items.
+// A per-launch choice rather than a branch in the kernel, whose scalar
+// registers would be the most any branch needs.
+template <bool FP8, int NG, bool SPLIT, int B = 1>
+void launch_matvec(const Geom &g, hipStream_t s, const void *d_x, const float *d_scale, float *d_y, float *partial,
+                   int64_t ldx = 0, int64_t ldy = 0) {
+  if constexpr (!SPLIT && B == 1 && NG <= 2) {
+    if (g.log2S == 5) return launch_matvec_ls<FP8, NG, SPLIT, B, 5>(g, s, d_x, d_scale, d_y, partial, ldx, ldy);
+    if (g.log2S == 6) return launch_matvec_ls<FP8, NG, SPLIT, B, 6>(g, s, d_x, d_scale, d_y, partial, ldx, ldy);
+  }
+  launch_matvec_ls<FP8, NG, SPLIT, B, -1>(g, s, d_x, d_scale, d_y, partial, ldx, ldy);
 }
 
 template <bool FP8>
@@ -1494,9 +1522,9 @@ void launch_matvec_c(const Geom &g, hipStream_t s, const void *d_x, const float 
 // the largest any member needs, padded as for one matrix.  The kernel derives
 // each matrix's row-sum slots per workgroup (ceil(groups / its workgroups))
 // the same way.
-template <bool FP8, int NG>
+template <bool FP8, int NG, int LS>
 void launch_group(const Geom *g, const nwc_matvec_desc *d, int count, hipStream_t s) {
-  const void *kernel = (const void *)matvec_group_kernel<FP8, NG>;
+  const void *kernel = (const void *)matvec_group_kernel<FP8, NG, LS>;
   const size_t static_lds = NWC_LUT_BYTES + (FP8 ? NWC_FP8_ESC_ENTRIES * 4 : 0);
   const uint32_t W = g[0].W, slot = W * g[0].R * 4;
   const uint32_t cap_slots = std::max<uint32_t>(1, 8192 / slot);
@@ -1541,17 +1569,27 @@ void launch_group(const Geom *g, const nwc_matvec_desc *d, int count, hipStream_
   const uint32_t begins = wide ? 0u : (count > 1 ? tail.begin[1] : 0u) | ((count > 2 ? tail.begin[2] : 0u) << 16);
   const uint8_t *b[3] = {tail.blob[0], count > 1 ? tail.blob[1] : tail.blob[0], count > 2 ? tail.blob[2] : tail.blob[0]};
   const uint16_t *xx[3] = {tail.x[0], count > 1 ? tail.x[1] : tail.x[0], count > 2 ? tail.x[2] : tail.x[0]};
-  hipLaunchKernelGGL((matvec_group_kernel<FP8, NG>), dim3(grid), dim3(W * 64), lds, s, head, begins, b[0], b[1], b[2],
+  hipLaunchKernelGGL((matvec_group_kernel<FP8, NG, LS>), dim3(grid), dim3(W * 64), lds, s, head, begins, b[0], b[1], b[2],
                      xx[0], xx[1], xx[2], tail);
+}
+
+// Kernels built for 32 or 64 lanes per row, as for one matrix.
+template <bool FP8, int NG>
+void launch_group_s(const Geom *g, const nwc_matvec_desc *d, int count, hipStream_t s) {
+  if constexpr (NG <= 2) {
+    if (g[0].log2S == 5) return launch_group<FP8, NG, 5>(g, d, count, s);
+    if (g[0].log2S == 6) return launch_group<FP8, NG, 6>(g, d, count, s);
+  }
+  launch_group<FP8, NG, -1>(g, d, count, s);
 }
 
 template <bool FP8>
 void launch_group_c(const Geom *g, const nwc_matvec_desc *d, int count, hipStream_t s) {
   switch (g[0].C) {
-    case 16: launch_group<FP8, 1>(g, d, count, s); break;
-    case 32: launch_group<FP8, 2>(g, d, count, s); break;
-    case 48: launch_group<FP8, 3>(g, d, count, s); break;
-    default: launch_group<FP8, 4>(g, d, count, s); break;
+    case 16: launch_group_s<FP8, 1>(g, d, count, s); break;
+    case 32: launch_group_s<FP8, 2>(g, d, count, s); break;
+    case 48: launch_group_s<FP8, 3>(g, d, count, s); break;
+    default: launch_group_s<FP8, 4>(g, d, count, s); break;
   }
 }
 

@@ -582,6 +582,10 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
   constexpr uint32_t kWinMax = FP8 ? 6u : 4u;  // longest item decoded from registers
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The table copy first: it needs nothing from memory, while the group
+  // count below may come from the blob's header (a scalar load the copy would
+  // otherwise wait for).
+  stage_lut(lut, s_lut, W, wave, lane);
   // Workgroup b takes groups b, b + grid, b + 2*grid, ...: at any time the
   // workgroups read neighbouring items, so the machine streams the planes in
   // order.
@@ -595,12 +599,11 @@ __device__ __forceinline__ void matvec_body(const uint32_t *__restrict__ items, 
   const uint32_t r = lane >> log2S, lane_c = (lane & (S - 1u)) * C;  // row in group, column in slice run
   const bool row_lane = (lane & (S - 1u)) == S - 1u;
 
-  stage_lut(lut, s_lut, W, wave, lane);
-  // Waits for the first item-table entry (and whatever else the caller read
-  // before this) here, once, right after the table copy is issued, instead of
-  // where the compiler would put the first use (after the activation loads,
-  // one memory round trip later).
-  asm volatile("" ::"s"(off0), "s"(rows0));
+  // Waits for the first item-table entry and the shape words (which the
+  // grouped kernel reads from the blob's header) here, once, right after the
+  // table copy is issued, instead of where the compiler would put the first
+  // use (after the start barrier, one memory round trip later).
+  asm volatile("" ::"s"(off0), "s"(rows0), "s"(a.r2s_lo), "s"(a.r2s_hi), "s"(a.R), "s"(a.region_words), "s"(a.n));
   if (FP8 && !a.huff) build_fp8_escapes(lds_addr(s_lut) + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
   // (row group, span) of the current group, stepped without a division.
   uint32_t rg = SPLIT ? first / a.n_spans : first, sp = first - rg * a.n_spans;
@@ -1841,6 +1844,14 @@ int nwc_matvec_group(const nwc_matvec_desc *mats, int count, void *stream) {
       ds[c] = mats[j];
       ++c;
     }
+    // Members in ascending order of row groups (stable).  Measured on MI355X
+    // (Qwen3-4B layers, medians of 5): q,k,v with q first 8.27 us, with q
+    // last 7.53 us.  Each output is the same in any order.
+    for (int i = 1; i < c; ++i)
+      for (int j = i; j > 0 && gs[j].n_rowgroups < gs[j - 1].n_rowgroups; --j) {
+        std::swap(gs[j], gs[j - 1]);
+        std::swap(ds[j], ds[j - 1]);
+      }
     if (h[m].elem == NWC_FP8_E4M3)
       launch_group_c<true>(gs, ds, c, s);
     else

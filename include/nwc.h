@@ -183,7 +183,8 @@ int nwc_matvec_noalloc(const void *header, const void *d_blob, const void *d_x, 
  *            or NULL, output); 1 <= count <= NWC_GROUP_MAX (0 does nothing).
  * Matrices of one work-item shape (element type, columns per lane, rows per
  * wave, waves per workgroup) share a launch; a group of several shapes is one
- * launch per shape, in order of first appearance.  Every output is bit-equal
+ * launch per shape, in order of first appearance (inside a launch the
+ * workgroups take the matrices smallest first).  Every output is bit-equal
  * to nwc_matvec on the same matrix and activation.  Matrices whose rows span
  * several workgroups (n_spans > 1) need a workspace and are refused
  * (NWC_ERR_UNSUPPORTED).  Outputs must not overlap each other or any input.

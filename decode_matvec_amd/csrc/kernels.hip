@@ -1829,7 +1829,7 @@ int nwc_matvec_group(const nwc_matvec_desc *mats, int count, void *stream) {
     if (h[m].n_spans != 1) return NWC_ERR_UNSUPPORTED;
     g[m] = make_geom(h[m], d.d_blob);
   }
-  // One launch per work-item shape, the shapes in their order of appearance.
+  // One launch per work-item shape, members in their order of appearance.
   hipStream_t s = (hipStream_t)stream;
   bool done[NWC_GROUP_MAX] = {};
   for (int m = 0; m < count; ++m) {

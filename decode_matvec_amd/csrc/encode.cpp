@@ -289,7 +289,12 @@ Geo auto_geo(int64_t n, int64_t k, int C_req, int R_req, const RowEstimate &est)
   double best_cost = 0;
   for (int C : Cs) {
     for (int R : Rs) {
-      const Geo g = make_geo(n, k, C, R, NWC_MAX_WAVES);
+      // 16 rows per wave is the matrix-core batch geometry: its workgroups
+      // keep at most 12 waves, so that two of them share a compute unit under
+      // the 25-wave cap (measured on MI355X, Qwen3-4B layer matrices at 8 /
+      // 16 / 32 tokens: 91.3 / 103.3 / 144.8 us per layer with up to 16 waves,
+      // 85.7 / 95.5 / 137.6 with up to 12, 98.1 / 105.5 / 136.8 with up to 8).
+      const Geo g = make_geo(n, k, C, R, R == 16 ? 12 : NWC_MAX_WAVES);
       if (C_req && R_req) return g;
       if (g.n_spans != 1) continue;
       if (nwc_lds_bytes_for(g.W, g.R, est.rows(C)) > NWC_LDS_BUDGET) continue;

@@ -558,7 +558,7 @@ def test_matvec_batch_matrix_cores(cols, batch):
     is never used; nothing written past a row's outputs."""
     from oracle import fast as F
     cases = [("ragged with rare values", S.inject_rare(S.student_t_bf16(91, (1000, 3001)), 92)),
-             ("q shape, rows over three spans", S.normal_bf16(93, (4096, 2560), float(np.float32(C.sigma_for(2560)))))]
+             ("q shape, rows over four spans", S.normal_bf16(93, (4096, 2560), float(np.float32(C.sigma_for(2560)))))]
     for what, w in cases:
         n, k = w.shape
         print(f"case mfma batch={batch} cols={cols} {what} {n}x{k}", flush=True)

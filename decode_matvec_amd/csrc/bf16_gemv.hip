@@ -36,6 +36,14 @@ __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
 
 // Sum of row `wr` (kc chunks of 8 BF16) against x; every lane of the wave
 // returns the row sum.
+// Weight loads are non-temporal like the compressed kernels' blob loads
+// (each weight is read once per call).
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+  const u32x4_nt v = __builtin_nontemporal_load((const u32x4_nt *)p);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
 __device__ __forceinline__ float row_dot(const uint4 *__restrict__ wr, const uint4 *__restrict__ x, uint32_t kc,
                                          uint32_t lane) {
   float a0 = 0.f, a1 = 0.f;
@@ -44,7 +52,7 @@ __device__ __forceinline__ float row_dot(const uint4 *__restrict__ wr, const uin
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const uint32_t c = c0 + u * 64 + lane;
-      wv[u] = c < kc ? wr[c] : make_uint4(0, 0, 0, 0);
+      wv[u] = c < kc ? ld_nt(wr + c) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {

@@ -101,6 +101,8 @@ int nwc_encode_bound(int64_t n, int64_t k, int elem, int cols_per_lane, int rows
  *            per lane stream (a lane's decode chain is cols_per_lane/2 steps).
  *   rows_per_wave: 0 = choose from the shape; else a power of two in [1, 64]:
  *            the rows one wave decodes, each split over 64/rows_per_wave lanes.
+ *            With 16 (the matrix-core geometry of nwc_matvec_batch) a
+ *            workgroup gets at most 12 waves, so that two share a compute unit.
  * Any BF16 pattern (NaN payloads, infinities, zeros, subnormals) and any fp8
  * byte is encoded losslessly.  Uses up to hardware_concurrency host threads. */
 int nwc_encode(const void *w_host, int64_t n, int64_t k, int64_t ld, int elem, int cols_per_lane,

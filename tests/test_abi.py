@@ -99,6 +99,18 @@ def test_two_span_geometry():
     assert info["n_items"] == 2 * 2 * 9
 
 
+def test_matrix_core_geometry_keeps_two_workgroups_per_cu():
+    # 16 rows per wave: at most 12 waves per workgroup (two fit under the 25-wave cap), the columns spread
+    # over as few spans as that allows; 2 rows of each shape keep the encode cheap.
+    for k, want in ((2560, (4, 10)), (4096, (6, 11)), (9728, (13, 12)), (1000, (2, 8))):
+        info = nwc.blob_info(nwc.encode(S.normal_bf16(k, (2, k), 0.02), cols_per_lane=16, rows_per_wave=16))
+        assert (info["n_spans"], info["waves_per_group"]) == want, k
+        assert info["n_spans"] * info["waves_per_group"] * 4 * 16 >= k
+    # other explicit geometries keep up to 16 waves
+    info = nwc.blob_info(nwc.encode(S.normal_bf16(9, (2, 4096), 0.02), cols_per_lane=16, rows_per_wave=4))
+    assert (info["n_spans"], info["waves_per_group"]) == (1, 16)
+
+
 def test_auto_geometry_of_the_layer_shapes():
     # Every Qwen3-4B projection gets a geometry whose row group fits one
     # workgroup (no span sums), stores at most 6% filler columns (K = 9728 =

@@ -1257,7 +1257,11 @@ __global__ __launch_bounds__(1024) void matvec_mfma_kernel(const uint32_t *__res
 // address is known: the id, then its item-table entry, then at once its code
 // words (a window's worth, zero past the item's rows: bounds-checked buffer
 // loads over the code plane) and its mantissa chunks, for every unit of the
-// thread before the one wait; the decode table is copied meanwhile.  Each
+// thread; the decode table is copied meanwhile.  The wait for the item-table
+// entries also drains the table copy, so a wave passes the start barrier with
+// its code words and mantissas still in flight and decodes its first unit as
+// soon as that unit's loads land (measured on MI355X, 4096 ids of 151936 x
+// 2560: 10.2 us against 10.5 with every load drained before the barrier).  Each
 // unit is then decoded from a register window sized to the longest item among
 // the wave's lanes, as the matvec does; a wave with an item longer than the
 // window copies each lane's stream to its LDS column and decodes from there.
@@ -1307,6 +1311,7 @@ __global__ __launch_bounds__(512) void gather_kernel(Geom g, const uint32_t *__r
     off[u] = items[2 * item[u]];
     rows[u] = items[2 * item[u] + 1];
   }
+  wait_vm0();  // the entries, and with them this wave's part of the table copy
   uint32_t w[U][kWinMax];
   uint4 m[U][NG];
 #pragma unroll
@@ -1322,7 +1327,6 @@ __global__ __launch_bounds__(512) void gather_kernel(Geom g, const uint32_t *__r
     }
   }
   if (FP8) build_fp8_escapes(lut + NWC_LUT_BYTES, threadIdx.x, blockDim.x);
-  wait_vm0();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   const int64_t esz = FP8 ? 1 : 2;
